@@ -1,0 +1,333 @@
+"""Pins of the CPU oracle against things other than itself: hand-derived golden
+cases, closed forms, brute force, an independent library routine (torch SDPA in
+float64) and invariants.  CPU only."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import KVCache
+from workloads import make_custom, make_score_vector
+from tests.conftest import load_golden
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------- golden
+
+def test_golden_attention_three_keys():
+    g = load_golden("attention_three_keys.json")
+    q = f32(g["q"])[None]                       # [B=1][N][Hq][D]
+    k = f32(g["k"])[:, None, :]                 # [slots][Hkv][D]
+    v = f32(g["v"])[:, None, :]
+    kv = KVCache(k, v, "f32", "contiguous", seq_stride=len(g["k"]))
+    P = np.array([g["P"]], dtype=np.int32)
+    out = oracle.verify_attention(q, "f32", kv, P, None, g["scale"], 1)
+    np.testing.assert_allclose(out[0], np.asarray(g["expect_out"]), rtol=0, atol=2e-6)
+    s = oracle.verify_scores(q, "f32", kv, P, [0], g["scale"], 1)
+    np.testing.assert_allclose(s[0], g["expect_scores"], rtol=0, atol=2e-6)
+    assert oracle.topk_select(s[0], g["P"], g["k_sel"]).tolist() == g["expect_idx"]
+
+
+def test_golden_tree_uniform():
+    g = load_golden("tree_uniform.json")
+    parent = np.asarray(g["parent"], dtype=np.int32)
+    N, D, P = len(parent), g["D"], g["P"]
+    for t, exp in enumerate(g["expect_ancestors"]):
+        assert sorted(oracle.ancestors(parent, t)) == exp
+    q = np.zeros((1, N, 1, D), dtype=np.float32)
+    k = np.ones((P + N, 1, D), dtype=np.float32)
+    v = np.zeros((P + N, 1, D), dtype=np.float32)
+    for j in range(P + N):
+        v[j, 0, j] = 6.0
+    kv = KVCache(k, v, "f32", "contiguous", seq_stride=P + N)
+    out = oracle.verify_attention(q, "f32", kv, np.array([P], np.int32), parent[None], 0.5, 1)
+    np.testing.assert_allclose(out[0, :, 0], np.asarray(g["expect_out"]), rtol=0, atol=1e-12)
+
+
+def test_golden_scores_small():
+    g = load_golden("scores_small.json")
+    q = f32(g["q"])[None]
+    P, N = g["P"], g["N"]
+    k = np.zeros((P + N, 1, g["D"]), dtype=np.float32)
+    k[:P, 0] = f32(g["k_prefix"])
+    k[P:, 0] = 1e6                               # verify tokens' keys: never scored
+    kv = KVCache(k, k, "f32", "contiguous", seq_stride=P + N)
+    for case in g["cases"]:
+        s = oracle.verify_scores(q, "f32", kv, np.array([P], np.int32), case["rows"], g["scale"], 1)
+        np.testing.assert_allclose(s[0], case["expect_scores"], rtol=0, atol=1e-12)
+        assert oracle.topk_select(s[0], P, case["k"]).tolist() == case["expect_idx"]
+
+
+def test_golden_topk_ties():
+    g = load_golden("topk_ties.json")
+    s = f32(g["scores"])
+    for case in g["cases"]:
+        assert oracle.topk_select(s, len(s), case["k"]).tolist() == case["expect_idx"], case
+
+
+def test_golden_sparse_two_keys():
+    g = load_golden("sparse_two_keys.json")
+    L, D = g["L"], g["D"]
+    k = np.tile(f32(g["fill_k"]), (L, 1, 1))
+    v = np.tile(f32(g["fill_v"]), (L, 1, 1))
+    for p, val in g["k_at"].items():
+        k[int(p), 0] = val
+    for p, val in g["v_at"].items():
+        v[int(p), 0] = val
+    kv = KVCache(k, v, "f32", "contiguous", seq_stride=L)
+    out = oracle.sparse_draft_attention(f32(g["q"])[None], "f32", kv, [np.array(g["idx"])], g["scale"], 1)
+    np.testing.assert_allclose(out[0], np.asarray(g["expect_out"]), rtol=0, atol=2e-6)
+
+
+# ----------------------------------------------------------------------------- library cross-check
+
+def _reach_mask(parent, N):
+    """Ancestor-or-self relation by boolean matrix closure (independent of the oracle's walk)."""
+    A = np.eye(N, dtype=bool)
+    for i in range(N):
+        if parent is None:
+            if i > 0:
+                A[i, i - 1] = True
+        elif parent[i] >= 0:
+            A[i, parent[i]] = True
+    R = A.copy()
+    for _ in range(N):
+        R2 = R | ((R.astype(np.int64) @ R.astype(np.int64)) > 0)
+        if (R2 == R).all():
+            break
+        R = R2
+    return R   # R[t, a]: a is t or an ancestor of t
+
+
+def _sdpa_verify(wl, b):
+    """torch scaled_dot_product_attention in float64 with an explicit boolean mask."""
+    kv = KVCache.of(wl)
+    Pb, N, G = int(wl.P[b]), wl.N, wl.Hq // wl.Hkv
+    L = Pb + N
+    slots = kv.slots(b, np.arange(L))
+    to64 = (lambda x: oracle.bf16_bits_to_f64(x)) if wl.dtype == "bf16" else (lambda x: x.astype(np.float64))
+    K = torch.from_numpy(to64(wl.k[slots])).permute(1, 0, 2)          # [Hkv][L][D]
+    V = torch.from_numpy(to64(wl.v[slots])).permute(1, 0, 2)
+    K = K.repeat_interleave(G, dim=0)                                 # MHA with repeated K/V
+    V = V.repeat_interleave(G, dim=0)
+    Q = torch.from_numpy(to64(wl.q[b])).permute(1, 0, 2)              # [Hq][N][D]
+    R = _reach_mask(None if wl.parent is None else wl.parent[b], N)
+    mask = np.zeros((N, L), dtype=bool)
+    mask[:, :Pb] = True
+    mask[:, Pb:] = R
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=torch.from_numpy(mask),
+                                                         scale=wl.scale)
+    return o.permute(1, 0, 2).numpy()                                 # [N][Hq][D]
+
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="f32", B=1, Hq=4, Hkv=1, D=64, P=300, N=5),
+    dict(dtype="bf16", B=2, Hq=8, Hkv=2, D=128, P=[200, 333], N=7, tree="best_first", tree_depth=4),
+    dict(dtype="bf16", B=1, Hq=4, Hkv=4, D=64, P=100, N=12, tree="best_first", tree_depth=3,
+         layout="paged", page_size=16),
+    dict(dtype="f32", B=1, Hq=6, Hkv=3, D=64, P=50, N=9, tree="best_first", tree_depth=8, q_std_mult=8.0),
+])
+def test_verify_matches_torch_sdpa(case):
+    wl = make_custom(seed=11, **case)
+    out = oracle.verify_attention(wl.q, wl.dtype, KVCache.of(wl), wl.P, wl.parent, wl.scale, wl.Hkv)
+    for b in range(wl.B):
+        np.testing.assert_allclose(out[b], _sdpa_verify(wl, b), rtol=1e-10, atol=1e-12)
+
+
+def test_chain_equals_triangular_mask():
+    wl = make_custom(seed=3, dtype="f32", Hq=2, Hkv=1, D=64, P=40, N=6, q_std_mult=10.0)
+    kv = KVCache.of(wl)
+    out = oracle.verify_attention(wl.q, "f32", kv, wl.P, None, wl.scale, 1)
+    # separately written causal mask: row t sees positions <= P + t
+    L = int(wl.P[0]) + wl.N
+    K = kv.keys(0, 0, np.arange(L))
+    V = kv.values(0, 0, np.arange(L))
+    tri = np.tril(np.ones((wl.N, wl.N), dtype=bool))
+    for t in range(wl.N):
+        vis = np.concatenate([np.ones(int(wl.P[0]), bool), tri[t]])
+        for h in range(2):
+            lg = wl.scale * (K[vis] @ wl.q[0, t, h].astype(np.float64))
+            w = np.exp(lg - lg.max())
+            np.testing.assert_allclose(out[0, t, h], (w / w.sum()) @ V[vis], rtol=1e-12, atol=1e-14)
+    # the same chain written as an explicit parent array gives the same result
+    out2 = oracle.verify_attention(wl.q, "f32", kv, wl.P, np.arange(-1, wl.N - 1)[None], wl.scale, 1)
+    np.testing.assert_array_equal(out, out2)
+
+
+# ----------------------------------------------------------------------------- closed forms / invariants
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", B=2, Hq=8, Hkv=2, D=64, P=[97, 130], N=6, score_rows=[0, 5]),
+    dict(dtype="f32", B=1, Hq=4, Hkv=1, D=64, P=77, N=5, score_rows="all"),
+    dict(dtype="bf16", B=1, Hq=8, Hkv=4, D=128, P=64, N=10, tree="best_first", score_rows=[1, 3, 4]),
+])
+def test_scores_closed_form(case):
+    """The sum of logits over rows and heads is linear in q: s_i = scale * sum_g K_g[i] . qbar_g."""
+    wl = make_custom(seed=5, **case)
+    s = oracle.verify_scores(wl.q, wl.dtype, KVCache.of(wl), wl.P, wl.score_rows, wl.scale, wl.Hkv)
+    G = wl.Hq // wl.Hkv
+    q = oracle.bf16_bits_to_f64(wl.q) if wl.dtype == "bf16" else wl.q.astype(np.float64)
+    kall = oracle.bf16_bits_to_f64(wl.k) if wl.dtype == "bf16" else wl.k.astype(np.float64)
+    for b in range(wl.B):
+        Pb = int(wl.P[b])
+        qbar = q[b][wl.score_rows].reshape(len(wl.score_rows), wl.Hkv, G, wl.D).sum(axis=(0, 2))
+        Kb = kall[b * wl.seq_stride: b * wl.seq_stride + Pb]          # [Pb][Hkv][D]
+        ref = wl.scale * np.einsum("igd,gd->i", Kb, qbar)
+        np.testing.assert_allclose(s[b, :Pb], ref, rtol=1e-10, atol=1e-12)
+        assert np.isnan(s[b, Pb:]).all()
+
+
+def test_scores_linear_in_rows_and_c2q_subset():
+    wl = make_custom(seed=9, dtype="bf16", Hq=8, Hkv=2, D=64, P=150, N=8)
+    kv = KVCache.of(wl)
+    f = lambda rows: oracle.verify_scores(wl.q, "bf16", kv, wl.P, rows, wl.scale, 2)  # noqa: E731
+    full = f(list(range(8)))
+    parts = sum(f([t]) for t in range(8))
+    np.testing.assert_allclose(full, parts, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(f([0, 7]), f([0]) + f([7]), rtol=1e-10, atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one():
+    wl = make_custom(seed=2, dtype="f32", Hq=4, Hkv=2, D=64, P=60, N=7, tree="best_first", q_std_mult=5.0)
+    wl.v[:] = 1.0
+    out = oracle.verify_attention(wl.q, "f32", KVCache.of(wl), wl.P, wl.parent, wl.scale, 2)
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-13)
+    dr = oracle.sparse_draft_attention(wl.dq[0], "f32", KVCache.of(wl), [np.arange(30)], wl.scale, 2)
+    np.testing.assert_allclose(dr, 1.0, rtol=0, atol=1e-13)
+
+
+def test_single_node_equals_decode_and_full_index_set():
+    """N = 1 verification is plain decode over prefix + self; the sparse draft
+    over every position reproduces it exactly (k = whole context == dense)."""
+    wl = make_custom(seed=4, dtype="bf16", B=2, Hq=8, Hkv=2, D=64, P=[120, 75], N=1, q_std_mult=4.0)
+    kv = KVCache.of(wl)
+    out = oracle.verify_attention(wl.q, "bf16", kv, wl.P, None, wl.scale, 2)
+    idx = [np.arange(int(wl.P[b]) + 1) for b in range(2)]
+    dr = oracle.sparse_draft_attention(wl.q[:, 0], "bf16", kv, idx, wl.scale, 2)
+    np.testing.assert_allclose(out[:, 0], dr, rtol=1e-12, atol=1e-14)
+
+
+def test_star_tree_is_prefix_root_self():
+    N = 6
+    star = np.array([-1] + [0] * (N - 1), dtype=np.int32)
+    wl = make_custom(seed=6, dtype="f32", Hq=2, Hkv=1, D=64, P=30, N=N, tree=star, q_std_mult=6.0)
+    kv = KVCache.of(wl)
+    out = oracle.verify_attention(wl.q, "f32", kv, wl.P, wl.parent, wl.scale, 1)
+    P = int(wl.P[0])
+    for t in range(N):
+        idx = np.concatenate([np.arange(P + 1), [P + t]]) if t else np.arange(P + 1)
+        dr = oracle.sparse_draft_attention(wl.q[:, t], "f32", kv, [idx], wl.scale, 1)
+        np.testing.assert_allclose(out[0, t], dr[0], rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_permutation_invariance_and_dense_prefix():
+    wl = make_custom(seed=8, dtype="bf16", Hq=8, Hkv=2, D=128, P=200, N=3, q_std_mult=5.0)
+    kv = KVCache.of(wl)
+    rng = np.random.default_rng(0)
+    idx = np.sort(rng.choice(200, 40, replace=False))
+    a = oracle.sparse_draft_attention(wl.dq[0], "bf16", kv, [idx], wl.scale, 2)
+    b = oracle.sparse_draft_attention(wl.dq[0], "bf16", kv, [rng.permutation(idx)], wl.scale, 2)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    # every prefix position selected == dense decode over the prefix (torch SDPA)
+    full = oracle.sparse_draft_attention(wl.dq[0], "bf16", kv, [np.arange(200)], wl.scale, 2)
+    K = torch.from_numpy(oracle.bf16_bits_to_f64(wl.k[:200])).permute(1, 0, 2).repeat_interleave(4, 0)
+    V = torch.from_numpy(oracle.bf16_bits_to_f64(wl.v[:200])).permute(1, 0, 2).repeat_interleave(4, 0)
+    Q = torch.from_numpy(oracle.bf16_bits_to_f64(wl.dq[0, 0]))[:, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=wl.scale)[:, 0].numpy()
+    np.testing.assert_allclose(full[0], ref, rtol=1e-10, atol=1e-13)
+    # empty index list gives zeros
+    z = oracle.sparse_draft_attention(wl.dq[0], "bf16", kv, [np.arange(0)], wl.scale, 2)
+    assert (z == 0).all()
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    wl = make_custom(seed=12, dtype="bf16", B=1, Hq=8, Hkv=2, D=64, P=90, N=6, tree="best_first",
+                     q_std_mult=4.0)
+    kv = KVCache.of(wl)
+    out = oracle.verify_attention(wl.q, "bf16", kv, wl.P, wl.parent, wl.scale, 2)
+    k_rep = np.repeat(wl.k, 4, axis=1)
+    v_rep = np.repeat(wl.v, 4, axis=1)
+    kv2 = KVCache(k_rep, v_rep, "bf16", "contiguous", wl.seq_stride)
+    out2 = oracle.verify_attention(wl.q, "bf16", kv2, wl.P, wl.parent, wl.scale, 8)
+    np.testing.assert_allclose(out, out2, rtol=1e-12, atol=1e-15)
+    s1 = oracle.verify_scores(wl.q, "bf16", kv, wl.P, wl.score_rows, wl.scale, 2)
+    s2 = oracle.verify_scores(wl.q, "bf16", kv2, wl.P, wl.score_rows, wl.scale, 8)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-14)
+
+
+def test_paged_equals_contiguous():
+    wl = make_custom(seed=13, dtype="bf16", B=3, Hq=4, Hkv=2, D=64, P=[50, 17, 80], N=5, tree="best_first")
+    kv = KVCache.of(wl)
+    # scatter the same logical tokens into a shuffled paged pool (written here, not by the generator)
+    ps = 8
+    rng = np.random.default_rng(1)
+    L = wl.P + wl.N
+    npg = (L + ps - 1) // ps
+    perm = rng.permutation(int(npg.sum()))
+    pt = np.full((3, int(npg.max())), -1, np.int32)
+    off = 0
+    kp = np.zeros((int(npg.sum()) * ps, 2, 64), np.uint16)
+    vp = np.zeros_like(kp)
+    for b in range(3):
+        pt[b, :npg[b]] = perm[off: off + npg[b]]
+        off += npg[b]
+        pos = np.arange(L[b])
+        sl = pt[b][pos // ps].astype(np.int64) * ps + pos % ps
+        kp[sl] = wl.k[b * wl.seq_stride + pos]
+        vp[sl] = wl.v[b * wl.seq_stride + pos]
+    kv2 = KVCache(kp, vp, "bf16", "paged", page_size=ps, page_table=pt)
+    o1 = oracle.verify_attention(wl.q, "bf16", kv, wl.P, wl.parent, wl.scale, 2)
+    o2 = oracle.verify_attention(wl.q, "bf16", kv2, wl.P, wl.parent, wl.scale, 2)
+    np.testing.assert_array_equal(o1, o2)
+    s1 = oracle.verify_scores(wl.q, "bf16", kv, wl.P, wl.score_rows, wl.scale, 2)
+    s2 = oracle.verify_scores(wl.q, "bf16", kv2, wl.P, wl.score_rows, wl.scale, 2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+# ----------------------------------------------------------------------------- selection brute force
+
+def _brute_topk(s, k):
+    """Explicit argmax over all k-subsets of the summed score (Vegas §2.A);
+    among maximisers, the lexicographically smallest ascending tuple."""
+    best, best_t = None, None
+    for t in itertools.combinations(range(len(s)), k):
+        v = sum(float(s[i]) for i in t)
+        if best is None or v > best:
+            best, best_t = v, t
+    return list(best_t) if best_t is not None else []
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_topk_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 13))
+    # integer-valued scores force exact ties; sums of integers are exact in float64
+    s = rng.integers(-3, 4, size=n).astype(np.float32)
+    for k in range(0, min(n, 5) + 1):
+        assert oracle.topk_select(s, n, k).tolist() == _brute_topk(s, k), (s, k)
+
+
+def test_topk_clamps_and_prefix_only():
+    s = make_score_vector(3, 50, "normal")
+    s[40:] = 1e9                      # entries past P_b must be ignored
+    got = oracle.topk_select(s, 40, 100)
+    assert got.tolist() == list(range(40))
+    got = oracle.topk_select(s, 40, 5)
+    assert len(got) == 5 and got.max() < 40 and (np.diff(got) > 0).all()
+
+
+def test_topk_signed_zero_and_wide():
+    s = make_score_vector(4, 200, "signed_zero")
+    got = oracle.topk_select(s, 200, 60)
+    # -0.0 and +0.0 tie: among zeros the lowest indices are taken regardless of sign
+    order = sorted(range(200), key=lambda i: (-float(s[i]), i))
+    assert got.tolist() == sorted(order[:60])
+    s = make_score_vector(5, 300, "wide")
+    got = oracle.topk_select(s, 300, 17)
+    thr = np.sort(s)[::-1][16]
+    assert (s[got] >= thr).all() and len(got) == 17
