@@ -1,0 +1,183 @@
+/*
+ * sv.h -- C ABI of the verification-attention hot path for MI355X (gfx950).
+ *
+ * One speculative-decoding iteration on one attention layer:
+ *
+ *   sv_verify_attn        full (dense) attention of the N verify queries of each
+ *                         sequence -- a linear draft chain or a draft tree whose
+ *                         nodes see only the prefix, their ancestors and
+ *                         themselves -- over the KV cache, plus one fp32
+ *                         criticality score per prefix entry: the pre-softmax
+ *                         logits summed over the chosen scoring rows and over
+ *                         all query heads.
+ *   sv_topk_select        the k highest-scoring prefix entries of each sequence.
+ *   sv_sparse_draft_attn  the next draft step's decode attention restricted to
+ *                         a gathered index set.
+ *
+ * Sources (technical-summary pages on gist.science/pt/paper/...):
+ *   Vegas (2602.07223): §2 "Mecanismo Central" steps 1-3 (verify with full
+ *     attention, select critical KV entries as a by-product, draft with sparse
+ *     attention over them); §2.A selection equation; §2.B Collect-2-Query;
+ *     §3 kernel instrumentation (pre-softmax logits) and sparse execution
+ *     (paged attention with one-token pages, token indices as page indices).
+ *   JETFLOW (2606.18394): §2 tree causal attention mask; §3 item 3 (paged
+ *     attention with a tree-mask stage).
+ *
+ * Conventions for every entry point:
+ *   - Pointers without a _host suffix are DEVICE pointers, owned by the caller.
+ *     The library never allocates, frees or retains them, and keeps no state
+ *     between calls (except the optional timing events, see below).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and performs no host synchronisation.  Host arrays (_host) are
+ *     read before the call returns.
+ *   - Results are deterministic: no floating-point atomics; re-running a call
+ *     on the same inputs gives bit-identical outputs.
+ *   - Host-visible arguments are validated before any launch; on error nothing
+ *     is launched, the status is returned and sv_last_error() describes it.
+ *     Contents of device arrays (prefix lengths, parents, page tables, index
+ *     lists) are a caller contract; kernels clamp positions so that they never
+ *     read outside the K/V storage described by sv_kv_cache.num_slots (a slot
+ *     outside [0, num_slots) reads as zeros).
+ */
+#ifndef SV_H
+#define SV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+typedef enum {
+  SV_OK = 0,
+  SV_E_INVALID = 1,      /* bad shape, null pointer, inconsistent sizes        */
+  SV_E_UNSUPPORTED = 2,  /* valid but not implemented: D not in {64,128}, N>256 */
+  SV_E_WORKSPACE = 3,    /* workspace missing or smaller than *_workspace_size */
+  SV_E_HIP = 4           /* a HIP runtime call or kernel launch failed          */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef void* sv_stream; /* hipStream_t */
+
+/* KV cache of one attention layer.
+ * K and V are token-major rows [slot][Hkv][D] of the call's dtype, D contiguous.
+ * Logical position i of sequence b lives in
+ *   contiguous (page_table == NULL): slot = b * seq_stride + i
+ *   paged:                            slot = page_table[b * max_pages + i / page_size] * page_size
+ *                                            + i % page_size
+ * For verification, the N verify tokens of sequence b have their K/V at
+ * logical positions [P_b, P_b + N) (they attend to themselves). */
+typedef struct {
+  const void* k;
+  const void* v;
+  const int32_t* page_table; /* device [B][max_pages], or NULL for contiguous */
+  int32_t page_size;         /* tokens per page (paged only), >= 1             */
+  int32_t max_pages;         /* row stride of page_table (paged only)          */
+  int64_t seq_stride;        /* slots per sequence (contiguous only)           */
+  int64_t num_slots;         /* number of [Hkv][D] rows in k and in v          */
+} sv_kv_cache;
+
+int sv_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* sv_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Verification attention + criticality scores.
+ *
+ * Vegas §2 step 1 and §5: every verify query attends with exact softmax
+ * attention to the whole prefix; JETFLOW §2: a tree node additionally sees its
+ * ancestors and itself among the verify tokens (never siblings or
+ * descendants).  Vegas §2.A / §3: the score of prefix entry i is
+ *     s[b][i] = sum_{t in score_rows} sum_{h < Hq} scale * q[b][t][h] . k[b][i][h / (Hq/Hkv)]
+ * i.e. pre-softmax logits summed over the scoring rows (all drafts, or the
+ * Collect-2-Query pair of Vegas §2.B) and over all query heads; rejected
+ * drafts count as well (the scores come from this pass alone).
+ *
+ *   q            [B][N][Hq][D] dtype; row t = verify node t (node 0 = root).
+ *   dtype        SV_F32 or SV_BF16 (q, K, V and out share it).
+ *   B, N, Hq, Hkv, D   batch, verify nodes (1..256), query heads, KV heads
+ *                (Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv)),
+ *                head dim (64 or 128).
+ *   kv           KV cache (see sv_kv_cache).
+ *   prefix_len   device int32[B]: P_b, committed prefix length (0 <= P_b <= P_max).
+ *   P_max        host scalar, >= every P_b; row stride of `scores`.
+ *   parent       device int32[B][N] draft-tree parents (parent[b][0] = -1,
+ *                0 <= parent[b][i] < i), or NULL for a linear chain (node i's
+ *                parent is i - 1, which is ordinary causal attention).
+ *   score_rows_host  host int32[n_score_rows], distinct nodes in [0, N) whose
+ *                logits are summed; n_score_rows = 0 means no scores.
+ *   softmax_scale    > 0, or 0 for 1/sqrt(D).
+ *   out          [B][N][Hq][D] dtype (round-to-nearest-even from fp32).
+ *   scores       fp32 [B][P_max]; entries i < P_b are written, the rest are
+ *                left untouched.  May be NULL iff n_score_rows == 0.
+ *   workspace    device scratch of at least sv_verify_workspace_size(...)
+ *                bytes (same B, N, Hq, Hkv, D, P_max, dtype, parent != NULL and
+ *                n_score_rows); contents on entry are ignored.
+ */
+size_t sv_verify_workspace_size(int B, int N, int Hq, int Hkv, int D, int P_max,
+                                sv_dtype dtype, int is_tree, int n_score_rows);
+sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                         const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                         const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,
+                         float softmax_scale, void* out, float* scores,
+                         void* workspace, size_t workspace_bytes, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Top-k selection (Vegas §2 step 2 and §2.A: the k-subset of the prefix with
+ * the largest summed score is the set of the k largest scores).
+ *
+ *   scores       fp32 [B][P_max] (only entries i < P_b are read).
+ *   prefix_len   device int32[B] (clamped to [0, P_max]).
+ *   k            device int32[B]: requested k_b; k'_b = min(k_b, P_b, k_max), >= 0.
+ *   k_max        host scalar: row stride of idx.
+ *   idx          device int32[B][k_max]: the k'_b selected indices in increasing
+ *                order, then -1 up to k_max.  Ties are broken toward the lower
+ *                index; -0.0 and +0.0 are equal.  Scores must be finite.
+ *   count        device int32[B] (may be NULL): k'_b.
+ *   workspace    sv_topk_workspace_size(B, P_max) bytes (may be 0 / NULL if that is 0).
+ */
+size_t sv_topk_workspace_size(int B, int P_max);
+sv_status sv_topk_select(const float* scores, int B, int P_max, const int32_t* prefix_len,
+                         const int32_t* k, int k_max, int32_t* idx, int32_t* count,
+                         void* workspace, size_t workspace_bytes, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse draft attention (Vegas §2 step 3 and §3: decode attention of one
+ * draft query per sequence over exactly the listed token positions, as a
+ * paged kernel whose pages hold one token and whose page indices are the
+ * token indices).
+ *
+ *   q            [B][Hq][D] dtype, one query per sequence.
+ *   kv           KV cache; idx entries are LOGICAL positions mapped through it
+ *                (so positions past the prefix -- accepted or drafted tokens --
+ *                may be listed too).
+ *   idx          device int32[B][idx_stride] logical positions.
+ *   n_idx        device int32[B]: entries of idx[b] to use (clamped to [0, max_idx]);
+ *                0 gives a zero output.  sv_topk_select's `count` fits here.
+ *   max_idx      host scalar >= every n_idx[b], <= idx_stride.
+ *   out          [B][Hq][D] dtype.
+ *   workspace    sv_sparse_workspace_size(B, Hq, Hkv, D, max_idx) bytes.
+ */
+size_t sv_sparse_workspace_size(int B, int Hq, int Hkv, int D, int max_idx);
+sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D,
+                               const sv_kv_cache* kv, const int32_t* idx, int idx_stride,
+                               const int32_t* n_idx, int max_idx, float softmax_scale, void* out,
+                               void* workspace, size_t workspace_bytes, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Optional timing hook for profiling: while set (non-NULL), every
+ * sv_verify_attn call on this thread records `start_event` on its stream right
+ * before its main attention kernel and `stop_event` right after it (both are
+ * hipEvent_t created by the caller).  Pass NULL, NULL to clear. */
+sv_status sv_set_verify_timing_events(void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H */

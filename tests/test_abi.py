@@ -1,0 +1,130 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before launching
+anything (validation makes no HIP call, so these run on a CPU-only host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_verify_sparse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libsv.so not built")
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_symbols()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_abi_version_and_empty_error():
+    lib = _lib.load()
+    assert lib.sv_abi_version() == 1
+    assert lib.sv_last_error() in (b"",) or isinstance(lib.sv_last_error(), bytes)
+
+
+def _kv(k=FAKE, v=FAKE, pt=None, ps=1, mp=0, stride=100, slots=1000):
+    return _lib.SvKvCache(k, v, pt, ps, mp, stride, slots)
+
+
+def _verify(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, dt=_lib.SV_BF16, B=1, N=8, Hq=32, Hkv=8, D=128, kv=_kv(), P=FAKE, P_max=32768,
+             parent=None, rows=[0, 7], scale=0.0, out=FAKE, scores=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    rows = a["rows"]
+    arr = (ctypes.c_int32 * max(1, len(rows)))(*rows) if rows is not None else None
+    if a["wsb"] == 0 and "wsb" not in kw:
+        a["wsb"] = lib.sv_verify_workspace_size(a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], a["P_max"], a["dt"],
+                                                int(a["parent"] is not None), len(rows or []))
+    st = lib.sv_verify_attn(a["q"], a["dt"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], ctypes.byref(a["kv"]),
+                            a["P"], a["P_max"], a["parent"], arr, len(rows or []) if "nrows" not in kw else kw["nrows"],
+                            a["scale"], a["out"], a["scores"], a["ws"], a["wsb"], a["stream"])
+    return st, lib.sv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(Hq=30), _lib.SV_E_INVALID, "multiple"),
+    (dict(D=96), _lib.SV_E_UNSUPPORTED, "head dim"),
+    (dict(N=257), _lib.SV_E_UNSUPPORTED, "exceeds"),
+    (dict(N=0), _lib.SV_E_INVALID, "N must"),
+    (dict(dt=7), _lib.SV_E_UNSUPPORTED, "dtype"),
+    (dict(rows=[0, 8]), _lib.SV_E_INVALID, "not in [0, N)"),
+    (dict(rows=[3, 3]), _lib.SV_E_INVALID, "twice"),
+    (dict(scores=None), _lib.SV_E_INVALID, "scores is NULL"),
+    (dict(q=None), _lib.SV_E_INVALID, "non-NULL"),
+    (dict(kv=_kv(k=None)), _lib.SV_E_INVALID, "kv.k"),
+    (dict(kv=_kv(slots=0)), _lib.SV_E_INVALID, "num_slots"),
+    (dict(kv=_kv(pt=FAKE, ps=0, mp=4)), _lib.SV_E_INVALID, "page_size"),
+    (dict(B=2, kv=_kv(stride=0)), _lib.SV_E_INVALID, "seq_stride"),
+    (dict(wsb=16), _lib.SV_E_WORKSPACE, "workspace"),
+    (dict(ws=None, wsb=1 << 40), _lib.SV_E_WORKSPACE, "workspace"),
+    (dict(scale=-1.0), _lib.SV_E_INVALID, "softmax_scale"),
+    (dict(scale=float("inf")), _lib.SV_E_INVALID, "softmax_scale"),
+    (dict(P_max=-1), _lib.SV_E_INVALID, "P_max"),
+])
+def test_verify_rejects_bad_arguments(kw, status, frag):
+    st, msg = _verify(**kw)
+    assert st == status, msg
+    assert frag in msg
+
+
+def test_verify_empty_batch_is_ok_without_launch():
+    st, msg = _verify(B=0, q=None, out=None)
+    assert st == _lib.SV_OK, msg
+
+
+def test_workspace_sizes_are_consistent():
+    lib = _lib.load()
+    chain = lib.sv_verify_workspace_size(1, 8, 32, 8, 128, 32768, _lib.SV_BF16, 0, 2)
+    tree = lib.sv_verify_workspace_size(1, 256, 32, 8, 128, 8192, _lib.SV_BF16, 1, 256)
+    assert chain > 32768 * 8 * 4 and tree > 0
+    assert lib.sv_verify_workspace_size(1, 257, 32, 8, 128, 10, _lib.SV_BF16, 0, 0) == 0
+    assert lib.sv_sparse_workspace_size(1, 32, 8, 128, 2048) >= 32 * 32 * 128 * 4
+    assert lib.sv_topk_workspace_size(4, 131072) == 0
+
+
+def test_topk_and_sparse_reject_bad_arguments():
+    lib = _lib.load()
+    assert lib.sv_topk_select(FAKE, -1, 10, FAKE, FAKE, 4, FAKE, None, None, 0, None) == _lib.SV_E_INVALID
+    assert lib.sv_topk_select(None, 1, 10, FAKE, FAKE, 4, FAKE, None, None, 0, None) == _lib.SV_E_INVALID
+    assert lib.sv_topk_select(FAKE, 0, 10, FAKE, FAKE, 4, FAKE, None, None, 0, None) == _lib.SV_OK
+    kv = _kv()
+    sp = lib.sv_sparse_draft_attn
+    assert sp(FAKE, _lib.SV_BF16, 1, 32, 8, 128, ctypes.byref(kv), FAKE, 10, FAKE, 20, 0.0, FAKE, FAKE, 1 << 30,
+              None) == _lib.SV_E_INVALID                       # max_idx > idx_stride
+    assert sp(FAKE, _lib.SV_BF16, 1, 32, 8, 100, ctypes.byref(kv), FAKE, 10, FAKE, 10, 0.0, FAKE, FAKE, 1 << 30,
+              None) == _lib.SV_E_UNSUPPORTED
+    assert sp(FAKE, _lib.SV_BF16, 1, 64, 2, 128, ctypes.byref(kv), FAKE, 10, FAKE, 10, 0.0, FAKE, FAKE, 1 << 30,
+              None) == _lib.SV_E_UNSUPPORTED                   # 32 query heads per KV head
+    assert sp(FAKE, _lib.SV_BF16, 1, 32, 8, 128, ctypes.byref(kv), FAKE, 10, FAKE, 10, 0.0, FAKE, FAKE, 8,
+              None) == _lib.SV_E_WORKSPACE
+    assert "workspace" in lib.sv_last_error().decode()
+
+
+def test_timing_events_must_pair():
+    lib = _lib.load()
+    assert lib.sv_set_verify_timing_events(FAKE, None) == _lib.SV_E_INVALID
+    assert lib.sv_set_verify_timing_events(None, None) == _lib.SV_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,199 @@
+"""Verification attention, top-k KV selection and sparse draft attention on MI355X.
+
+Python binding of libsv.so (include/sv.h).  Every step runs in the library's
+HIP kernels; this module only marshals torch tensors (device memory and the
+current stream) into the C ABI.  Importing works without a GPU; calling
+requires the built library and a gfx950 device, and there is no fallback.
+
+    out, scores = verify_attn(q, kv, prefix_len, parent=None, score_rows=[0, N-1])
+    idx, count  = topk_select(scores, prefix_len, k, k_max)
+    draft_out   = sparse_draft_attn(q1, kv, idx, count)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import SvError, SV_F32, SV_BF16  # noqa: F401
+
+__all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn",
+           "verify_workspace_size", "sparse_workspace_size", "timing_events", "SvError", "lib"]
+
+
+def lib() -> ctypes.CDLL:
+    return _lib.load()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the HIP library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the HIP library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+@dataclasses.dataclass
+class KVCache:
+    """K/V of one layer, token-major [num_slots][Hkv][D] each.
+
+    Contiguous (page_table None): slot of (b, i) = b * seq_stride + i.
+    Paged: slot = page_table[b][i // page_size] * page_size + i % page_size.
+    """
+    k: torch.Tensor
+    v: torch.Tensor
+    seq_stride: int = 0
+    page_table: Optional[torch.Tensor] = None
+    page_size: int = 1
+
+    def c_struct(self) -> _lib.SvKvCache:
+        if self.k.shape != self.v.shape or self.k.dim() != 3:
+            raise ValueError("k and v must both be [num_slots][Hkv][D]")
+        pt = self.page_table
+        return _lib.SvKvCache(
+            _ptr(self.k), _ptr(self.v), _ptr(pt) if pt is not None else None,
+            int(self.page_size) if pt is not None else 1,
+            int(pt.shape[1]) if pt is not None else 0,
+            int(self.seq_stride), int(self.k.shape[0]))
+
+    @property
+    def Hkv(self) -> int:
+        return int(self.k.shape[1])
+
+    @property
+    def D(self) -> int:
+        return int(self.k.shape[2])
+
+
+class Workspace:
+    """Reusable device scratch buffer (grown on demand, never shrunk)."""
+
+    def __init__(self, device=None):
+        self.buf: Optional[torch.Tensor] = None
+        self.device = device
+
+    def get(self, nbytes: int, device) -> tuple[Optional[int], int]:
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf.data_ptr(), self.buf.numel()
+
+
+_default_ws: dict = {}
+
+
+def _ws(workspace: Optional[Workspace], key: str) -> Workspace:
+    if workspace is not None:
+        return workspace
+    return _default_ws.setdefault(key, Workspace())
+
+
+def verify_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, is_tree, n_score_rows) -> int:
+    return int(lib().sv_verify_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, int(bool(is_tree)), n_score_rows))
+
+
+def sparse_workspace_size(B, Hq, Hkv, D, max_idx) -> int:
+    return int(lib().sv_sparse_workspace_size(B, Hq, Hkv, D, max_idx))
+
+
+def verify_attn(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max: int,
+                parent: Optional[torch.Tensor] = None, score_rows: Optional[Sequence[int]] = None,
+                scale: float = 0.0, out: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                workspace: Optional[Workspace] = None):
+    """sv_verify_attn: q [B][N][Hq][D] -> (out [B][N][Hq][D], scores fp32 [B][P_max] or None).
+
+    ``score_rows``: verify nodes whose logits are summed into the scores
+    (None or [] = no scores).  ``parent``: int32 [B][N] draft tree or None (chain).
+    """
+    L = lib()
+    B, N, Hq, D = (int(x) for x in q.shape)
+    rows = [int(r) for r in (score_rows or [])]
+    if out is None:
+        out = torch.empty_like(q)
+    if rows and scores is None:
+        scores = torch.empty((B, P_max), dtype=torch.float32, device=q.device)
+    rows_arr = (ctypes.c_int32 * max(1, len(rows)))(*rows)
+    dt = _dtype_code(q)
+    nbytes = verify_workspace_size(B, N, Hq, kv.Hkv, D, P_max, dt, parent is not None, len(rows))
+    wptr, wlen = _ws(workspace, "verify").get(nbytes, q.device)
+    kvs = kv.c_struct()
+    _lib.check(L.sv_verify_attn(_ptr(q), dt, B, N, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(prefix_len), P_max,
+                                _ptr(parent), rows_arr, len(rows), float(scale), _ptr(out),
+                                _ptr(scores) if rows else None, wptr, wlen, _stream(q.device)))
+    return out, (scores if rows else None)
+
+
+def topk_select(scores: torch.Tensor, prefix_len: torch.Tensor, k: torch.Tensor, k_max: int,
+                idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None):
+    """sv_topk_select: -> (idx int32 [B][k_max] ascending, -1 padded; count int32 [B])."""
+    L = lib()
+    B, P_max = (int(x) for x in scores.shape)
+    if idx is None:
+        idx = torch.empty((B, k_max), dtype=torch.int32, device=scores.device)
+    if count is None:
+        count = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    _lib.check(L.sv_topk_select(_ptr(scores), B, P_max, _ptr(prefix_len), _ptr(k), k_max, _ptr(idx), _ptr(count),
+                                None, 0, _stream(scores.device)))
+    return idx, count
+
+
+def sparse_draft_attn(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, n_idx: torch.Tensor, *,
+                      max_idx: Optional[int] = None, scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[Workspace] = None):
+    """sv_sparse_draft_attn: q [B][Hq][D], idx int32 [B][stride] logical positions, n_idx int32 [B]."""
+    L = lib()
+    B, Hq, D = (int(x) for x in q.shape)
+    stride = int(idx.shape[1])
+    max_idx = stride if max_idx is None else int(max_idx)
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _dtype_code(q)
+    nbytes = sparse_workspace_size(B, Hq, kv.Hkv, D, max_idx)
+    wptr, wlen = _ws(workspace, "sparse").get(nbytes, q.device)
+    kvs = kv.c_struct()
+    _lib.check(L.sv_sparse_draft_attn(_ptr(q), dt, B, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(idx), stride,
+                                      _ptr(n_idx), max_idx, float(scale), _ptr(out), wptr, wlen,
+                                      _stream(q.device)))
+    return out
+
+
+class timing_events:
+    """Context manager: record (start, stop) hipEvents around the main verify
+    kernel of every sv_verify_attn call made inside it (on the call's stream)."""
+
+    def __init__(self, start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+        for e in (start, stop):
+            if e.cuda_event == 0:   # torch creates its events lazily
+                e.record()
+        self.start, self.stop = start, stop
+
+    def __enter__(self):
+        _lib.check(lib().sv_set_verify_timing_events(self.start.cuda_event, self.stop.cuda_event))
+        return self
+
+    def __exit__(self, *exc):
+        _lib.check(lib().sv_set_verify_timing_events(None, None))
+        return False
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

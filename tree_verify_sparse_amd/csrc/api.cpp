@@ -1,0 +1,178 @@
+// C ABI of the verification-attention library: argument validation, workspace
+// sizing and kernel launches.  Validation touches no HIP API, so every error
+// path can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sv.h"
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local void* g_ev_start = nullptr;
+thread_local void* g_ev_stop = nullptr;
+
+sv_status fail(sv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sv_status ok() {
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
+sv_status check_heads(int Hq, int Hkv, int D) {
+  if (Hq <= 0 || Hkv <= 0) return fail(SV_E_INVALID, "Hq (%d) and Hkv (%d) must be positive", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(SV_E_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (D != 64 && D != 128) return fail(SV_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+  return SV_OK;
+}
+
+sv_status check_kv(const sv_kv_cache* kv, int B) {
+  if (!kv) return fail(SV_E_INVALID, "kv is NULL");
+  if (!kv->k || !kv->v) return fail(SV_E_INVALID, "kv.k / kv.v is NULL");
+  if (kv->num_slots <= 0) return fail(SV_E_INVALID, "kv.num_slots must be positive");
+  if (kv->page_table) {
+    if (kv->page_size <= 0) return fail(SV_E_INVALID, "kv.page_size must be >= 1 for a paged cache");
+    if (kv->max_pages <= 0) return fail(SV_E_INVALID, "kv.max_pages must be >= 1 for a paged cache");
+  } else {
+    if (kv->seq_stride < 0) return fail(SV_E_INVALID, "kv.seq_stride must be >= 0");
+    if (B > 1 && kv->seq_stride == 0) return fail(SV_E_INVALID, "kv.seq_stride is 0 with B > 1");
+  }
+  return SV_OK;
+}
+
+sv_status check_dtype(sv_dtype dt) {
+  if (dt != SV_F32 && dt != SV_BF16) return fail(SV_E_UNSUPPORTED, "dtype %d not supported", (int)dt);
+  return SV_OK;
+}
+
+float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / sqrtf((float)D); }
+
+sv::KvArgs kv_args(const sv_kv_cache* kv) {
+  return sv::KvArgs{kv->k, kv->v, kv->page_table, kv->page_size, kv->max_pages,
+                    (long long)kv->seq_stride, (long long)kv->num_slots};
+}
+
+sv_status hip_status(int e, const char* what) {
+  if (e != 0) return fail(SV_E_HIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_last_error(void) { return g_err; }
+
+sv_status sv_set_verify_timing_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(SV_E_INVALID, "timing events must be both set or both NULL");
+  g_ev_start = start_event;
+  g_ev_stop = stop_event;
+  return ok();
+}
+
+size_t sv_verify_workspace_size(int B, int N, int Hq, int Hkv, int D, int P_max, sv_dtype dtype,
+                                int is_tree, int n_score_rows) {
+  if (B <= 0 || N <= 0 || N > sv::kMaxNodes || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (D != 64 && D != 128) ||
+      P_max < 0 || n_score_rows < 0)
+    return 0;
+  return sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, is_tree != 0, n_score_rows).bytes;
+}
+
+sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                         const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                         const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,
+                         float softmax_scale, void* out, float* scores, void* workspace,
+                         size_t workspace_bytes, sv_stream stream) {
+  sv_status st;
+  if ((st = check_dtype(dtype))) return st;
+  if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
+  if (N <= 0) return fail(SV_E_INVALID, "N must be >= 1");
+  if (N > sv::kMaxNodes) return fail(SV_E_UNSUPPORTED, "N = %d verify nodes exceeds %d", N, sv::kMaxNodes);
+  if ((st = check_heads(Hq, Hkv, D))) return st;
+  if (P_max < 0) return fail(SV_E_INVALID, "P_max must be >= 0");
+  if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return fail(SV_E_INVALID, "softmax_scale must be finite and >= 0");
+  if (n_score_rows < 0 || n_score_rows > N) return fail(SV_E_INVALID, "n_score_rows = %d not in [0, N]", n_score_rows);
+  if (n_score_rows > 0) {
+    if (!score_rows_host) return fail(SV_E_INVALID, "score_rows_host is NULL");
+    if (!scores) return fail(SV_E_INVALID, "scores is NULL but n_score_rows > 0");
+    unsigned char seen[sv::kMaxNodes] = {0};
+    for (int i = 0; i < n_score_rows; ++i) {
+      const int t = score_rows_host[i];
+      if (t < 0 || t >= N) return fail(SV_E_INVALID, "score row %d = %d not in [0, N)", i, t);
+      if (seen[t]) return fail(SV_E_INVALID, "score row %d listed twice", t);
+      seen[t] = 1;
+    }
+  }
+  if (B == 0) return ok();
+  if (!q || !out || !prefix_len) return fail(SV_E_INVALID, "q, out and prefix_len must be non-NULL");
+  if ((st = check_kv(kv, B))) return st;
+  const sv::VerifyPlan p = sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, parent != nullptr, n_score_rows);
+  if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
+    return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
+  const int e = sv::launch_verify(p, q, kv_args(kv), prefix_len, parent, score_rows_host, n_score_rows,
+                                  resolve_scale(softmax_scale, D), out, scores, workspace, stream, g_ev_start,
+                                  g_ev_stop);
+  return hip_status(e, "sv_verify_attn launch");
+}
+
+size_t sv_topk_workspace_size(int B, int P_max) {
+  (void)B;
+  (void)P_max;
+  return 0;
+}
+
+sv_status sv_topk_select(const float* scores, int B, int P_max, const int32_t* prefix_len, const int32_t* k,
+                         int k_max, int32_t* idx, int32_t* count, void* workspace, size_t workspace_bytes,
+                         sv_stream stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B < 0 || P_max < 0 || k_max < 0) return fail(SV_E_INVALID, "B, P_max and k_max must be >= 0");
+  if (B == 0) return ok();
+  if (!scores || !prefix_len || !k || (!idx && k_max > 0))
+    return fail(SV_E_INVALID, "scores, prefix_len, k and idx must be non-NULL");
+  return hip_status(sv::launch_topk(scores, B, P_max, prefix_len, k, k_max, idx, count, stream),
+                    "sv_topk_select launch");
+}
+
+size_t sv_sparse_workspace_size(int B, int Hq, int Hkv, int D, int max_idx) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (D != 64 && D != 128) || max_idx < 0) return 0;
+  return sv::plan_sparse(B, Hq, Hkv, D, max_idx).bytes;
+}
+
+sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D,
+                               const sv_kv_cache* kv, const int32_t* idx, int idx_stride, const int32_t* n_idx,
+                               int max_idx, float softmax_scale, void* out, void* workspace,
+                               size_t workspace_bytes, sv_stream stream) {
+  sv_status st;
+  if ((st = check_dtype(dtype))) return st;
+  if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
+  if ((st = check_heads(Hq, Hkv, D))) return st;
+  if (Hq / Hkv > 16) return fail(SV_E_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (max_idx < 0 || idx_stride < max_idx) return fail(SV_E_INVALID, "need 0 <= max_idx <= idx_stride");
+  if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return fail(SV_E_INVALID, "softmax_scale must be finite and >= 0");
+  if (B == 0) return ok();
+  if (!q || !out || !n_idx || (!idx && max_idx > 0)) return fail(SV_E_INVALID, "q, out, idx and n_idx must be non-NULL");
+  if ((st = check_kv(kv, B))) return st;
+  const sv::SparsePlan p = sv::plan_sparse(B, Hq, Hkv, D, max_idx);
+  if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
+    return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
+  return hip_status(sv::launch_sparse(p, (int)dtype, q, kv_args(kv), idx, idx_stride, n_idx,
+                                      resolve_scale(softmax_scale, D), out, workspace, stream),
+                    "sv_sparse_draft_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// Sparse draft attention: one decode query per sequence attends to exactly a
+// gathered list of KV positions (Vegas §2 step 3; §3: a paged attention kernel
+// whose pages hold a single token, with token indices used as page indices).
+//
+// One 256-thread workgroup per (sequence, KV head, chunk of kChunk listed
+// positions): it gathers the chunk's K and V rows of that head (each a
+// contiguous D-element row, so every gather is whole 128-byte lines) into LDS,
+// forms the logits of the G query heads sharing the KV head, and writes a
+// partial (m, l, o) per query head.  A second kernel merges the chunks with
+// log-sum-exp weights.  The work is a few FLOP per byte, so it runs on the
+// vector ALUs; the gathers are what costs.
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kChunk = 64;
+constexpr int kMaxG = 16;
+
+struct SparseArgs {
+  const void* q;
+  void* out;
+  KvView kv;
+  const int32_t* idx;
+  const int32_t* n_idx;
+  float* ws_o;
+  f32x2* ws_ml;
+  int B, Hq, Hkv, G, idx_stride, max_idx, n_chunks;
+  float scale_log2;
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int CPR = ROWB / 16;
+  constexpr int KSTR = D + 1;  // fp32 row stride in LDS (floats): one bank per key
+  __shared__ float qs[kMaxG][D];
+  __shared__ float Ks[kChunk][KSTR];
+  __shared__ float Vs[kChunk][D];
+  __shared__ float lg[kMaxG][kChunk];
+  __shared__ float mls[kMaxG][2];
+
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  int n = a.n_idx[b];
+  n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
+  const int k0 = c * kChunk;
+  if (k0 >= n) return;
+  const int nk = min(kChunk, n - k0);
+  const int G = a.G;
+
+  for (int e = tid; e < G * D; e += 256) {
+    const int j = e / D, d = e % D;
+    qs[j][d] = (float)reinterpret_cast<const T*>(a.q)[((long long)b * a.Hq + g * G + j) * D + d];
+  }
+  // gather K/V rows of the listed positions (16-byte pieces, widened to fp32 in LDS)
+  const char* kb = reinterpret_cast<const char*>(a.kv.k) + (long long)g * ROWB;
+  const char* vb = reinterpret_cast<const char*>(a.kv.v) + (long long)g * ROWB;
+  const long long sb = (long long)a.Hkv * ROWB;
+  for (int e = tid; e < kChunk * CPR; e += 256) {
+    const int key = e / CPR, col = e % CPR;
+    long long s = -1;
+    if (key < nk) s = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + k0 + key]);
+    uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+    if (s >= 0) {
+      kx = *reinterpret_cast<const uint4*>(kb + s * sb + col * 16);
+      vx = *reinterpret_cast<const uint4*>(vb + s * sb + col * 16);
+    }
+    constexpr int EPC = 16 / (int)sizeof(T);
+    const T* kt = reinterpret_cast<const T*>(&kx);
+    const T* vt = reinterpret_cast<const T*>(&vx);
+#pragma unroll
+    for (int u = 0; u < EPC; ++u) {
+      Ks[key][col * EPC + u] = (float)kt[u];
+      Vs[key][col * EPC + u] = (float)vt[u];
+    }
+  }
+  __syncthreads();
+
+  // logits, one (head, key) pair per thread
+  for (int e = tid; e < G * kChunk; e += 256) {
+    const int j = e / kChunk, key = e % kChunk;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) acc += qs[j][d] * Ks[key][d];
+    lg[j][key] = key < nk ? acc * a.scale_log2 : kNegInf;
+  }
+  __syncthreads();
+
+  // softmax statistics per head: one wave per head, one lane per key
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int j = wave; j < G; j += 4) {
+    const float x = lg[j][lane];
+    const float mx = wave_max(x);
+    const float p = x == kNegInf ? 0.f : fast_exp2(x - mx);
+    const float ls = wave_sum(p);
+    lg[j][lane] = p;
+    if (lane == 0) {
+      mls[j][0] = mx;
+      mls[j][1] = ls;
+    }
+  }
+  __syncthreads();
+
+  // P V, one (head, column) pair per thread
+  for (int e = tid; e < G * D; e += 256) {
+    const int j = e / D, d = e % D;
+    float acc = 0.f;
+    for (int key = 0; key < nk; ++key) acc += lg[j][key] * Vs[key][d];
+    const long long rec = ((long long)b * a.Hq + g * G + j) * a.n_chunks + c;
+    a.ws_o[rec * D + d] = acc;
+    if (d == 0) a.ws_ml[rec] = f32x2{mls[j][0], mls[j][1]};
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + wave;
+  if (bh >= a.B * a.Hq) return;
+  const int b = bh / a.Hq;
+  int n = a.n_idx[b];
+  n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
+  const int nc = (n + kChunk - 1) / kChunk;
+  const long long rec0 = (long long)bh * a.n_chunks;
+  float M = kNegInf;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.ws_ml[rec0 + c][0]);
+  constexpr int PER = D / 64;
+  float acc[PER] = {};
+  float lsum = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const f32x2 ml = a.ws_ml[rec0 + c];
+    const float wt = M == kNegInf ? 0.f : fast_exp2(ml[0] - M);
+    lsum += wt * ml[1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += wt * a.ws_o[(rec0 + c) * D + lane * PER + e];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  T* dst = reinterpret_cast<T*>(a.out) + (long long)bh * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) dst[e] = (T)(acc[e] * inv);
+}
+
+SparsePlan plan_sparse(int B, int Hq, int Hkv, int D, int max_idx) {
+  SparsePlan p{};
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.D = D; p.max_idx = max_idx;
+  p.KCH = kChunk;
+  p.n_chunks = (max_idx + kChunk - 1) / kChunk;
+  if (p.n_chunks < 1) p.n_chunks = 1;
+  size_t off = 0;
+  p.off_o = off; off = align_up(off + (size_t)B * Hq * p.n_chunks * D * 4);
+  p.off_ml = off; off = align_up(off + (size_t)B * Hq * p.n_chunks * 8);
+  p.bytes = off;
+  return p;
+}
+
+template <typename T, int D>
+static void launch_sparse_typed(const SparsePlan& p, const SparseArgs& a, hipStream_t st) {
+  if (p.max_idx > 0)
+    hipLaunchKernelGGL((sparse_partial<T, D>), dim3(p.n_chunks, p.Hkv, p.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sparse_merge<T, D>), dim3((p.B * p.Hq + 3) / 4), dim3(256), 0, st, a);
+}
+
+int launch_sparse(const SparsePlan& p, int dtype, const void* q, const KvArgs& kv, const int32_t* idx,
+                  int idx_stride, const int32_t* n_idx, float scale, void* out, void* ws, void* stream) {
+  SparseArgs a{};
+  a.q = q;
+  a.out = out;
+  a.kv = KvView{kv.k, kv.v, kv.page_table, kv.page_size, kv.max_pages, kv.seq_stride, kv.num_slots};
+  a.idx = idx;
+  a.n_idx = n_idx;
+  char* w = reinterpret_cast<char*>(ws);
+  a.ws_o = reinterpret_cast<float*>(w + p.off_o);
+  a.ws_ml = reinterpret_cast<f32x2*>(w + p.off_ml);
+  a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.idx_stride = idx_stride; a.max_idx = p.max_idx;
+  a.n_chunks = p.n_chunks;
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (p.B == 0 || p.Hq == 0) return 0;
+  if (dtype == SV_BF16) {
+    if (p.D == 128) launch_sparse_typed<bf16, 128>(p, a, st);
+    else launch_sparse_typed<bf16, 64>(p, a, st);
+  } else {
+    if (p.D == 128) launch_sparse_typed<float, 128>(p, a, st);
+    else launch_sparse_typed<float, 64>(p, a, st);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,87 @@
+// Device-side building blocks for gfx950 (CDNA4): vector types, MFMA wrappers,
+// LDS transpose reads and small cross-lane helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+// C/D layout of the 32x32 MFMAs (checked on gfx950): lane l holds column l % 32;
+// element v holds row 8*(v/4) + 4*(l/32) + v%4.
+__device__ __forceinline__ int mfma_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  // A: lane l holds row l%32, k = 8*(l/32) + [0,8); B: column l%32, same k.
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+  // A: lane l holds row l%32, k = l/32; B: column l%32, k = l/32.
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4e+c supplies the address of 4 consecutive 16-bit elements; lane j of
+// the group receives, as its element e, element (j % 4) of lane 4e + j/4.
+// With lane 4e+c pointing at row (base+e), columns [4c, 4c+4) of a row-major
+// tile, lane j gets column j of rows base..base+3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)p));
+  bf16x4 out;
+  __builtin_memcpy(&out, &r, sizeof(out));
+  return out;
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// exp2 that maps -inf to 0 without NaN for (-inf) - (-inf) callers guard.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// K/V storage addressing: logical position -> slot; out-of-range -> -1.
+struct KvView {
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  int page_size;
+  int max_pages;
+  long long seq_stride;
+  long long num_slots;
+
+  __device__ __forceinline__ long long slot(int b, int pos) const {
+    long long s;
+    if (page_table == nullptr) {
+      s = (long long)b * seq_stride + pos;
+    } else {
+      int pg = pos / page_size;
+      if (pg < 0 || pg >= max_pages) return -1;
+      int phys = page_table[(long long)b * max_pages + pg];
+      s = (long long)phys * page_size + (pos - pg * page_size);
+    }
+    return (s >= 0 && s < num_slots && pos >= 0) ? s : -1;
+  }
+};
+
+}  // namespace sv

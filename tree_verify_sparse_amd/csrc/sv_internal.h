@@ -1,0 +1,58 @@
+// Host-side plans shared by the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sv.h"
+
+namespace sv {
+
+constexpr int kMaxNodes = 256;       // verify nodes per sequence
+constexpr int kAncWords = 8;         // ancestor bitset words per node (256 bits)
+constexpr int kInlineQbarRows = 64;  // scoring (row, head) pairs summed inside the main kernel
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// How one sv_verify_attn call is split into workgroups and workspace regions.
+struct VerifyPlan {
+  int B, N, Hq, Hkv, G, D, P_max, dtype;
+  int R;            // query rows per KV head = N * G (row = node * G + head-in-group)
+  int RT, WR, WK;   // row tiles per wave, waves along rows, waves along keys (WR*WK = 4)
+  int rows_per_block, RB, Rpad;
+  int TK;           // keys per LDS tile
+  int chunk;        // keys per split of the KV range
+  int n_chunks;     // splits covering the longest sequence (P_max + N)
+  int n_wg;         // workgroups of the main kernel (multiple of 8)
+  bool tree, scores, prep_qbar, prep;
+  size_t off_o, off_ml, off_s, off_qbar, off_anc, bytes;
+};
+
+VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtype, bool tree,
+                       int n_score_rows);
+
+struct SparsePlan {
+  int B, Hq, Hkv, G, D, max_idx, KCH, n_chunks;
+  size_t off_o, off_ml, bytes;
+};
+SparsePlan plan_sparse(int B, int Hq, int Hkv, int D, int max_idx);
+
+struct KvArgs {
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  int page_size, max_pages;
+  long long seq_stride, num_slots;
+};
+
+// Launchers (return a hipError_t as int; 0 = success).
+int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const int32_t* prefix_len,
+                  const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
+                  void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop);
+int launch_topk(const float* scores, int B, int P_max, const int32_t* prefix_len, const int32_t* k,
+                int k_max, int32_t* idx, int32_t* count, void* stream);
+int launch_sparse(const SparsePlan& p, int dtype, const void* q, const KvArgs& kv, const int32_t* idx,
+                  int idx_stride, const int32_t* n_idx, float scale, void* out, void* ws, void* stream);
+
+}  // namespace sv
