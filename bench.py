@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the verification-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+sv_verify_attn (dense tree/chain verification + fused criticality scores) ->
+sv_topk_select -> sv_sparse_draft_attn (one draft query per sequence, or the
+workload's number of draft steps over the same selected set).
+
+Default workload: the 32k-context Llama-3-8B-shaped layer (B=1, 32 query /
+8 KV heads, D=128, bf16, prefix 32768, chain of 8 verify queries,
+Collect-2-Query scoring, k=2048, one sparse draft step).
+
+Prints ONE JSON line.  `value` is the whole step's algorithmic bytes divided
+by the measured step time (GB/s); `roofline` is for the dominant kernel (the
+verify main kernel), timed with HIP events recorded on its own stream around
+each launch inside the timed region; `cpu_baseline` is the CPU oracle timed on
+a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+F32_MFMA_PEAK_TFS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kv-copies", type=int, default=0,
+                    help="KV copies rotated between steps so that no step hits the 256 MB MALL (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_verify_sparse_amd as sv
+    from tree_verify_sparse_amd import _lib
+    from workloads import make_workload, CONFIG_NAMES
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = sv.lib()
+
+    wl = make_workload(args.workload, args.seed)
+    es = 2 if wl.dtype == "bf16" else 4
+    n_draft = int(wl.dq.shape[0])
+
+    def to_dev(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+    kv_bytes = wl.k.nbytes + wl.v.nbytes
+    copies = args.kv_copies or max(1, min(8, int(np.ceil(600e6 / kv_bytes))))
+    k0, v0 = to_dev(wl.k), to_dev(wl.v)
+    kcs = [k0] + [k0.clone() for _ in range(copies - 1)]
+    vcs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    q = to_dev(wl.q)
+    dqs = [to_dev(wl.dq[s]) for s in range(n_draft)]
+    P = i32(wl.P)
+    ksel = i32(wl.k_sel)
+    parent = i32(wl.parent) if wl.parent is not None else None
+    pt = i32(wl.page_table) if wl.page_table is not None else None
+    out = torch.empty_like(q)
+    scores = torch.empty((wl.B, wl.P_max), dtype=torch.float32, device=dev)
+    kmax = wl.k_max
+    idx = torch.empty((wl.B, kmax), dtype=torch.int32, device=dev)
+    count = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    douts = [torch.empty_like(d) for d in dqs]
+    dt = _lib.SV_BF16 if wl.dtype == "bf16" else _lib.SV_F32
+    rows = [int(r) for r in wl.score_rows]
+    rows_arr = (ctypes.c_int32 * max(1, len(rows)))(*rows)
+    vws_n = sv.verify_workspace_size(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, wl.P_max, dt, parent is not None, len(rows),
+                                     wl.page_size if pt is not None else 0)
+    sws_n = sv.sparse_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, kmax)
+    vws = torch.empty(max(1, vws_n), dtype=torch.uint8, device=dev)
+    sws = torch.empty(max(1, sws_n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    # prebuilt C arguments, one set per KV copy (keeps per-step host work to three C calls)
+    kvs = [_lib.SvKvCache(kc.data_ptr(), vc.data_ptr(), pt.data_ptr() if pt is not None else None,
+                          wl.page_size if pt is not None else 1, wl.max_pages, wl.seq_stride, wl.num_slots)
+           for kc, vc in zip(kcs, vcs)]
+    vargs = [(q.data_ptr(), dt, wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, ctypes.byref(kv), P.data_ptr(), wl.P_max,
+              parent.data_ptr() if parent is not None else None, rows_arr, len(rows), 0.0, out.data_ptr(),
+              scores.data_ptr(), vws.data_ptr(), vws_n, sp) for kv in kvs]
+    targs = (scores.data_ptr(), wl.B, wl.P_max, P.data_ptr(), ksel.data_ptr(), kmax, idx.data_ptr(),
+             count.data_ptr(), None, 0, sp)
+    dargs = [[(dqs[s].data_ptr(), dt, wl.B, wl.Hq, wl.Hkv, wl.D, ctypes.byref(kv), idx.data_ptr(), kmax,
+               count.data_ptr(), kmax, 0.0, douts[s].data_ptr(), sws.data_ptr(), sws_n, sp)
+              for s in range(n_draft)] for kv in kvs]
+    f_verify, f_topk, f_sparse, f_hook = L.sv_verify_attn, L.sv_topk_select, L.sv_sparse_draft_attn, \
+        L.sv_set_verify_timing_events
+
+    def step(i, ev=None):
+        c = i % copies
+        if ev is not None:
+            f_hook(ev[0].cuda_event, ev[1].cuda_event)
+        st = f_verify(*vargs[c])
+        st |= f_topk(*targs)
+        for a in dargs[c]:
+            st |= f_sparse(*a)
+        if st:
+            raise RuntimeError(L.sv_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in kev:        # torch creates events lazily: force creation before handing them to the library
+        a.record()
+        b.record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(K):
+        step(i, kev[i])
+    e1.record()
+    torch.cuda.synchronize()
+    f_hook(None, None)
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / K
+    k_ms = [a.elapsed_time(b) for a, b in kev]
+    kern_ms = float(np.mean(k_ms))
+
+    # ---- algorithmic work
+    Pb = wl.P.astype(np.int64)
+    kk = np.minimum(wl.k_sel.astype(np.int64), Pb)
+    row_b = wl.Hkv * wl.D * es
+    verify_bytes = int((Pb + wl.N).sum() * row_b * 2 + wl.q.nbytes * 2 + (Pb.sum() * 4 if rows else 0))
+    select_bytes = int(Pb.sum() * 4 + kk.sum() * 4) if rows else 0
+    draft_bytes = int(n_draft * (kk.sum() * row_b * 2 + 2 * wl.B * wl.Hq * wl.D * es + kk.sum() * 4))
+    step_bytes = verify_bytes + select_bytes + draft_bytes
+    # verify flops: QK^T and PV over every visible key of every query row
+    vis = 0
+    for b in range(wl.B):
+        depth = np.zeros(wl.N, np.int64)
+        for t in range(1, wl.N):
+            depth[t] = depth[(t - 1) if wl.parent is None else wl.parent[b, t]] + 1
+        vis += int(wl.N * Pb[b] + (depth + 1).sum())
+    verify_flops = 4 * wl.Hq * wl.D * vis
+
+    mfma_bound = wl.N * (wl.Hq // wl.Hkv) >= 256  # wide trees: dense contraction
+    if mfma_bound:
+        peak = BF16_MFMA_PEAK_TFS if wl.dtype == "bf16" else F32_MFMA_PEAK_TFS
+        achieved = verify_flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = verify_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = "verify_main"
+    roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    roof["algorithmic_bytes"] = verify_bytes
+    roof["algorithmic_flops"] = verify_flops
+    roof["traffic"] = _traffic(args.workload)
+
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": "verify+select+sparse-draft us/step and HBM GB/s (% peak) at 32k ctx, 1 GPU",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded; no model weights or datasets)",
+        "config": {"workload": CONFIG_NAMES[args.workload], "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D,
+                   "prefix": int(wl.P_max) if wl.B == 1 else [int(x) for x in wl.P], "verify_nodes": wl.N,
+                   "tree": wl.parent is not None, "score_rows": len(rows), "k": int(wl.k_sel.max()),
+                   "draft_steps": n_draft, "paged": wl.layout == "paged", "kv_copies_rotated": copies,
+                   "step_bytes": step_bytes, "parallelism": "single-gpu"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline and args.workload in (1, 2, 3):
+        res["cpu_baseline"] = cpu_baseline(wl, step_bytes, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def _traffic(workload: int):
+    """HBM bytes per verify launch from the committed rocprofv3 counter summary,
+    only if the verify kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"verify_pmc_workload{workload}.md")
+    src = os.path.join(ROOT, "tree_verify_sparse_amd", "csrc", "verify.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        m = re.search(r"verify\.hip sha256:\s*([0-9a-f]{64})", text)
+        t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+        if m and t and m.group(1) == sha:
+            return float(t.group(1))
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, step_bytes, target_s):
+    """The CPU oracle (unchanged, float64 numpy) timed on this host: full steps
+    of the same workload, repeated until about target_s seconds have passed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.run_step(wl)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el / reps * (reps + 1) > 3 * target_s:
+            break
+    per = el / reps
+    return {"value": round(step_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds_per_step": round(per, 3), "numpy": np.__version__,
+            "host_cpus": os.cpu_count(),
+            "sample": f"{reps} full step(s) of the same workload (all verify rows, scores, top-k, "
+                      f"{wl.dq.shape[0]} draft step(s))"}
+
+
+if __name__ == "__main__":
+    main()

@@ -35,9 +35,10 @@
  *   - Host-visible arguments are validated before any launch; on error nothing
  *     is launched, the status is returned and sv_last_error() describes it.
  *     Contents of device arrays (prefix lengths, parents, page tables, index
- *     lists) are a caller contract; kernels clamp positions so that they never
- *     read outside the K/V storage described by sv_kv_cache.num_slots (a slot
- *     outside [0, num_slots) reads as zeros).
+ *     lists) are a caller contract.  Kernels never access K/V outside the
+ *     storage described by sv_kv_cache.num_slots: a position whose slot falls
+ *     outside [0, num_slots) is read from slot 0 instead, and results that
+ *     depend on it are unspecified.
  */
 #ifndef SV_H
 #define SV_H
@@ -116,11 +117,12 @@ const char* sv_last_error(void);
  *   scores       fp32 [B][P_max]; entries i < P_b are written, the rest are
  *                left untouched.  May be NULL iff n_score_rows == 0.
  *   workspace    device scratch of at least sv_verify_workspace_size(...)
- *                bytes (same B, N, Hq, Hkv, D, P_max, dtype, parent != NULL and
- *                n_score_rows); contents on entry are ignored.
+ *                bytes (same B, N, Hq, Hkv, D, P_max, dtype, parent != NULL,
+ *                n_score_rows and kv->page_size, or 0 for a contiguous cache);
+ *                contents on entry are ignored.
  */
 size_t sv_verify_workspace_size(int B, int N, int Hq, int Hkv, int D, int P_max,
-                                sv_dtype dtype, int is_tree, int n_score_rows);
+                                sv_dtype dtype, int is_tree, int n_score_rows, int page_size);
 sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
                          const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
                          const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,

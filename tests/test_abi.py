@@ -51,7 +51,7 @@ def _verify(**kw):
     arr = (ctypes.c_int32 * max(1, len(rows)))(*rows) if rows is not None else None
     if a["wsb"] == 0 and "wsb" not in kw:
         a["wsb"] = lib.sv_verify_workspace_size(a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], a["P_max"], a["dt"],
-                                                int(a["parent"] is not None), len(rows or []))
+                                                int(a["parent"] is not None), len(rows or []), 0)
     st = lib.sv_verify_attn(a["q"], a["dt"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], ctypes.byref(a["kv"]),
                             a["P"], a["P_max"], a["parent"], arr, len(rows or []) if "nrows" not in kw else kw["nrows"],
                             a["scale"], a["out"], a["scores"], a["ws"], a["wsb"], a["stream"])
@@ -91,10 +91,14 @@ def test_verify_empty_batch_is_ok_without_launch():
 
 def test_workspace_sizes_are_consistent():
     lib = _lib.load()
-    chain = lib.sv_verify_workspace_size(1, 8, 32, 8, 128, 32768, _lib.SV_BF16, 0, 2)
-    tree = lib.sv_verify_workspace_size(1, 256, 32, 8, 128, 8192, _lib.SV_BF16, 1, 256)
+    chain = lib.sv_verify_workspace_size(1, 8, 32, 8, 128, 32768, _lib.SV_BF16, 0, 2, 0)
+    tree = lib.sv_verify_workspace_size(1, 256, 32, 8, 128, 8192, _lib.SV_BF16, 1, 256, 0)
     assert chain > 32768 * 8 * 4 and tree > 0
-    assert lib.sv_verify_workspace_size(1, 257, 32, 8, 128, 10, _lib.SV_BF16, 0, 0) == 0
+    assert lib.sv_verify_workspace_size(1, 257, 32, 8, 128, 10, _lib.SV_BF16, 0, 0, 0) == 0
+    # small pages shorten chunks (the page-table slice of a chunk is cached on chip): more partials
+    p1 = lib.sv_verify_workspace_size(2, 8, 32, 8, 128, 65536, _lib.SV_BF16, 0, 2, 1)
+    p16 = lib.sv_verify_workspace_size(2, 8, 32, 8, 128, 65536, _lib.SV_BF16, 0, 2, 16)
+    assert p1 > p16 > 0
     assert lib.sv_sparse_workspace_size(1, 32, 8, 128, 2048) >= 32 * 32 * 128 * 4
     assert lib.sv_topk_workspace_size(4, 131072) == 0
 

@@ -107,8 +107,9 @@ def _ws(workspace: Optional[Workspace], key: str) -> Workspace:
     return _default_ws.setdefault(key, Workspace())
 
 
-def verify_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, is_tree, n_score_rows) -> int:
-    return int(lib().sv_verify_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, int(bool(is_tree)), n_score_rows))
+def verify_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, is_tree, n_score_rows, page_size=0) -> int:
+    return int(lib().sv_verify_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, int(bool(is_tree)), n_score_rows,
+                                              int(page_size)))
 
 
 def sparse_workspace_size(B, Hq, Hkv, D, max_idx) -> int:
@@ -133,7 +134,8 @@ def verify_attn(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max
         scores = torch.empty((B, P_max), dtype=torch.float32, device=q.device)
     rows_arr = (ctypes.c_int32 * max(1, len(rows)))(*rows)
     dt = _dtype_code(q)
-    nbytes = verify_workspace_size(B, N, Hq, kv.Hkv, D, P_max, dt, parent is not None, len(rows))
+    nbytes = verify_workspace_size(B, N, Hq, kv.Hkv, D, P_max, dt, parent is not None, len(rows),
+                                   kv.page_size if kv.page_table is not None else 0)
     wptr, wlen = _ws(workspace, "verify").get(nbytes, q.device)
     kvs = kv.c_struct()
     _lib.check(L.sv_verify_attn(_ptr(q), dt, B, N, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(prefix_len), P_max,

@@ -58,7 +58,7 @@ def load() -> ctypes.CDLL:
     lib.sv_last_error.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
     lib.sv_verify_workspace_size.restype = sz
-    lib.sv_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.sv_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.sv_verify_attn.restype = i32
     lib.sv_verify_attn.argtypes = [vp, i32, i32, i32, i32, i32, i32, kvp, vp, i32, vp, vp, i32, f32,
                                    vp, vp, vp, sz, vp]

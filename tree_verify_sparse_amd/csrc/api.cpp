@@ -85,11 +85,11 @@ sv_status sv_set_verify_timing_events(void* start_event, void* stop_event) {
 }
 
 size_t sv_verify_workspace_size(int B, int N, int Hq, int Hkv, int D, int P_max, sv_dtype dtype,
-                                int is_tree, int n_score_rows) {
+                                int is_tree, int n_score_rows, int page_size) {
   if (B <= 0 || N <= 0 || N > sv::kMaxNodes || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (D != 64 && D != 128) ||
-      P_max < 0 || n_score_rows < 0)
+      P_max < 0 || n_score_rows < 0 || page_size < 0)
     return 0;
-  return sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, is_tree != 0, n_score_rows).bytes;
+  return sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, is_tree != 0, n_score_rows, page_size).bytes;
 }
 
 sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
@@ -120,7 +120,8 @@ sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, in
   if (B == 0) return ok();
   if (!q || !out || !prefix_len) return fail(SV_E_INVALID, "q, out and prefix_len must be non-NULL");
   if ((st = check_kv(kv, B))) return st;
-  const sv::VerifyPlan p = sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, parent != nullptr, n_score_rows);
+  const sv::VerifyPlan p = sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, parent != nullptr, n_score_rows,
+                                           kv->page_table ? kv->page_size : 0);
   if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
     return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
   const int e = sv::launch_verify(p, q, kv_args(kv), prefix_len, parent, score_rows_host, n_score_rows,

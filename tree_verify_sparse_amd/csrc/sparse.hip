@@ -32,11 +32,13 @@ struct SparseArgs {
 template <typename T, int D>
 __global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
   constexpr int ROWB = D * (int)sizeof(T);
-  constexpr int CPR = ROWB / 16;
-  constexpr int KSTR = D + 1;  // fp32 row stride in LDS (floats): one bank per key
-  __shared__ float qs[kMaxG][D];
-  __shared__ float Ks[kChunk][KSTR];
-  __shared__ float Vs[kChunk][D];
+  constexpr int CPR = ROWB / 16;              // 16-byte pieces per row
+  constexpr int LOADS = kChunk * CPR / 256;   // pieces per thread per tensor
+  constexpr int EPC = 16 / (int)sizeof(T);    // elements per piece
+  constexpr int KSTR = D + EPC;               // LDS row stride (elements): +16 bytes spreads banks
+  __shared__ __attribute__((aligned(16))) T Ks[kChunk][KSTR];
+  __shared__ __attribute__((aligned(16))) T Vs[kChunk][D];
+  __shared__ __attribute__((aligned(16))) float qs[kMaxG][D];
   __shared__ float lg[kMaxG][kChunk];
   __shared__ float mls[kMaxG][2];
 
@@ -48,40 +50,43 @@ __global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
   const int nk = min(kChunk, n - k0);
   const int G = a.G;
 
+  // gather: every load of the chunk is issued before any is used
+  const char* kb = reinterpret_cast<const char*>(a.kv.k) + (long long)g * ROWB;
+  const char* vb = reinterpret_cast<const char*>(a.kv.v) + (long long)g * ROWB;
+  const long long sb = (long long)a.Hkv * ROWB;
+  uint4 kx[LOADS], vx[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int e = tid + 256 * i, key = e / CPR, col = e % CPR;
+    long long s = -1;
+    if (key < nk) s = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + k0 + key]);
+    if (s < 0) s = 0;  // unused or unmapped entries read slot 0 and are masked below
+    kx[i] = *reinterpret_cast<const uint4*>(kb + s * sb + col * 16);
+    vx[i] = *reinterpret_cast<const uint4*>(vb + s * sb + col * 16);
+  }
   for (int e = tid; e < G * D; e += 256) {
     const int j = e / D, d = e % D;
     qs[j][d] = (float)reinterpret_cast<const T*>(a.q)[((long long)b * a.Hq + g * G + j) * D + d];
   }
-  // gather K/V rows of the listed positions (16-byte pieces, widened to fp32 in LDS)
-  const char* kb = reinterpret_cast<const char*>(a.kv.k) + (long long)g * ROWB;
-  const char* vb = reinterpret_cast<const char*>(a.kv.v) + (long long)g * ROWB;
-  const long long sb = (long long)a.Hkv * ROWB;
-  for (int e = tid; e < kChunk * CPR; e += 256) {
-    const int key = e / CPR, col = e % CPR;
-    long long s = -1;
-    if (key < nk) s = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + k0 + key]);
-    uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-    if (s >= 0) {
-      kx = *reinterpret_cast<const uint4*>(kb + s * sb + col * 16);
-      vx = *reinterpret_cast<const uint4*>(vb + s * sb + col * 16);
-    }
-    constexpr int EPC = 16 / (int)sizeof(T);
-    const T* kt = reinterpret_cast<const T*>(&kx);
-    const T* vt = reinterpret_cast<const T*>(&vx);
 #pragma unroll
-    for (int u = 0; u < EPC; ++u) {
-      Ks[key][col * EPC + u] = (float)kt[u];
-      Vs[key][col * EPC + u] = (float)vt[u];
-    }
+  for (int i = 0; i < LOADS; ++i) {
+    const int e = tid + 256 * i, key = e / CPR, col = e % CPR;
+    *reinterpret_cast<uint4*>(&Ks[key][col * EPC]) = kx[i];
+    *reinterpret_cast<uint4*>(&Vs[key][col * EPC]) = vx[i];
   }
   __syncthreads();
 
-  // logits, one (head, key) pair per thread
+  // logits: one (head, key) pair per thread, 16-byte LDS reads
   for (int e = tid; e < G * kChunk; e += 256) {
     const int j = e / kChunk, key = e % kChunk;
     float acc = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < D; ++d) acc += qs[j][d] * Ks[key][d];
+#pragma unroll
+    for (int cc = 0; cc < CPR; ++cc) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(&Ks[key][cc * EPC]);
+      const T* kt = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) acc += qs[j][cc * EPC + u] * (float)kt[u];
+    }
     lg[j][key] = key < nk ? acc * a.scale_log2 : kNegInf;
   }
   __syncthreads();
@@ -101,17 +106,26 @@ __global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
   }
   __syncthreads();
 
-  // P V, one (head, column) pair per thread
-  for (int e = tid; e < G * D; e += 256) {
-    const int j = e / D, d = e % D;
-    float acc = 0.f;
-    for (int key = 0; key < nk; ++key) acc += lg[j][key] * Vs[key][d];
+  // P V: one (head, column pair) per thread
+  for (int e = tid; e < G * (D / 2); e += 256) {
+    const int j = e / (D / 2), d = 2 * (e % (D / 2));
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
+    for (int key = 0; key < nk; ++key) {
+      const float p = lg[j][key];
+      a0 += p * (float)Vs[key][d];
+      a1 += p * (float)Vs[key][d + 1];
+    }
     const long long rec = ((long long)b * a.Hq + g * G + j) * a.n_chunks + c;
-    a.ws_o[rec * D + d] = acc;
+    *reinterpret_cast<f32x2*>(a.ws_o + rec * D + d) = f32x2{a0, a1};
     if (d == 0) a.ws_ml[rec] = f32x2{mls[j][0], mls[j][1]};
   }
 }
 
+// Chunk merge: one wave per (sequence, query head).  The pair's partials are
+// contiguous ([chunk][D] floats), so the wave fetches up to 256 / (D / 4)
+// chunks per round with one 16-byte load per lane per step, every load issued
+// before any is used; lanes holding the same columns are then summed.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -123,21 +137,41 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   const int nc = (n + kChunk - 1) / kChunk;
   const long long rec0 = (long long)bh * a.n_chunks;
   float M = kNegInf;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.ws_ml[rec0 + c][0]);
-  constexpr int PER = D / 64;
-  float acc[PER] = {};
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, a.ws_ml[rec0 + c][0]);
+  M = wave_max(M);
+  constexpr int Q4 = D / 4;          // float4 column groups per row
+  constexpr int CPL = 64 / Q4;       // chunks covered by one wave-wide load step
+  constexpr int STEPS = 8;           // load steps in flight per round
+  const int quad = lane % Q4, sub = lane / Q4;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const f32x2 ml = a.ws_ml[rec0 + c];
-    const float wt = M == kNegInf ? 0.f : fast_exp2(ml[0] - M);
-    lsum += wt * ml[1];
+  for (int cb = 0; cb < nc; cb += CPL * STEPS) {
+    f32x4 x[STEPS];
+    float w[STEPS];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += wt * a.ws_o[(rec0 + c) * D + lane * PER + e];
+    for (int j = 0; j < STEPS; ++j) {
+      const int c = cb + j * CPL + sub;
+      x[j] = c < nc ? *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * quad) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x2 ml = c < nc ? a.ws_ml[rec0 + c] : f32x2{kNegInf, 0.f};
+      w[j] = (M == kNegInf || c >= nc) ? 0.f : fast_exp2(ml[0] - M);
+      if (quad == 0) lsum += w[j] * ml[1];
+    }
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) acc += w[j] * x[j];
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  T* dst = reinterpret_cast<T*>(a.out) + (long long)bh * D + lane * PER;
+  // lanes with the same quad (different sub) hold different chunks: sum them
 #pragma unroll
-  for (int e = 0; e < PER; ++e) dst[e] = (T)(acc[e] * inv);
+  for (int o = Q4; o < 64; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], o);
+  }
+  lsum = wave_sum(lsum);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if (sub == 0) {
+    T* dst = reinterpret_cast<T*>(a.out) + (long long)bh * D + 4 * quad;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = (T)(acc[e] * inv);
+  }
 }
 
 SparsePlan plan_sparse(int B, int Hq, int Hkv, int D, int max_idx) {

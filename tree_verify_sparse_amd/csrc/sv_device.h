@@ -57,8 +57,34 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// exp2 that maps -inf to 0 without NaN for (-inf) - (-inf) callers guard.
+// 2^x on the transcendental unit (2^-inf = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all its LDS operations are done (s_waitcnt vmcnt(N) lgkmcnt(0)).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies (the
+// fence would make the compiler drain every outstanding global->LDS copy).
+// Callers order memory explicitly with wait_vm_lgkm0 first.
+__device__ __forceinline__ void barrier_only() { __builtin_amdgcn_s_barrier(); }
+
+// Copy 16 bytes per lane from global memory straight into LDS: lane l writes
+// lds_base + 16*l (lds_base is wave-uniform).  Counted by vmcnt.  Issued as
+// inline assembly on purpose: the compiler then does not know that LDS is
+// written asynchronously and adds no vmcnt(0) drains before LDS reads that it
+// cannot prove disjoint from the copy; callers order the copies themselves
+// with wait_vm_lgkm0 + barrier_only (compiler-issued loads that are older
+// than these copies stay correctly waited for, since completion is in order).
+__device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src) : "memory");
+}
 
 // K/V storage addressing: logical position -> slot; out-of-range -> -1.
 struct KvView {

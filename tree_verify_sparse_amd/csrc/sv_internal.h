@@ -29,8 +29,9 @@ struct VerifyPlan {
   size_t off_o, off_ml, off_s, off_qbar, off_anc, bytes;
 };
 
+// page_size: tokens per page of a paged cache, 0 for a contiguous cache.
 VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtype, bool tree,
-                       int n_score_rows);
+                       int n_score_rows, int page_size);
 
 struct SparsePlan {
   int B, Hq, Hkv, G, D, max_idx, KCH, n_chunks;

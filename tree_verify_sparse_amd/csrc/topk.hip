@@ -2,13 +2,17 @@
 // sequence (Vegas §2 step 2 and §2.A: the k-subset with the largest summed
 // score is the set of the k largest scores).
 //
-// Scores map to order-preserving 32-bit keys (-0.0 folded onto +0.0).  Four
-// 8-bit radix passes over the keys find the exact key tau of the k-th largest
-// entry and how many entries equal to tau are still needed; a final pass in
-// index order keeps every key > tau and the lowest-index keys == tau, and a
-// block-wide scan writes the kept indices in increasing order.  Histograms
-// use integer LDS atomics, so the result does not depend on thread timing.
-// Rows of up to kCache entries are read from memory once and kept in LDS.
+// Scores map to order-preserving 32-bit keys (-0.0 folded onto +0.0).  The
+// offsets x = key - min_key are then radix-selected from the most significant
+// bit of (max_key - min_key) downward, 11 bits per pass, which finds the exact
+// key tau of the k-th largest entry and how many entries equal to tau are
+// still needed.  Starting the digits at the top of the occupied key range
+// (rather than at bit 31, where sign and exponent bits put nearly all scores
+// into a few bins) keeps the LDS histogram atomics spread out.  A final pass
+// in index order keeps every key > tau and the lowest-index keys == tau, and a
+// block-wide scan writes them in increasing index order.  Histograms use
+// integer LDS atomics, so the result does not depend on thread timing.  Rows
+// of up to kCache entries are read from memory once and kept in LDS.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -16,6 +20,7 @@ namespace sv {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kCache = 32768;
+constexpr int kBins = 2048;  // 11-bit digits: 2 bins per thread in the bucket scan
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -52,13 +57,20 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* sh, ui
   return r;
 }
 
+// Keys of elements [base, base + kTopkThreads * 32) are handled 32 per thread:
+// element base + 4 * (tid + kTopkThreads * j) + e, j < 8, e < 4 (coalesced float4 loads).
+constexpr int kPerThread = 32;
+constexpr int kRound = kTopkThreads * kPerThread;
+
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ scores, int P_max,
                                                            const int32_t* __restrict__ prefix_len,
                                                            const int32_t* __restrict__ kreq, int k_max,
                                                            int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-  __shared__ uint32_t cache[kCache];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[20];
+  // key i lives at cache[i + i / 32]: a thread reading its 32 consecutive keys
+  // and the 64 lanes of a wave then hit 64 different banks
+  __shared__ uint32_t cache[kCache + kCache / 32];
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sh[24];
   const int b = blockIdx.x, tid = threadIdx.x;
   int P = prefix_len[b];
   P = P < 0 ? 0 : (P > P_max ? P_max : P);
@@ -74,87 +86,139 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
     return;
   }
   const bool cached = P <= kCache;
+  const bool vec = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
 
-  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+  // 32 keys per thread per round: element base + 4 * (tid + kTopkThreads * j) + e (coalesced)
+  auto elem = [&](int base, int j, int e) { return base + 4 * (tid + kTopkThreads * j) + e; };
+  auto load_round = [&](int base, uint32_t (&u)[kPerThread]) {
+#pragma unroll
+    for (int j = 0; j < kPerThread / 4; ++j) {
+      const int i0 = elem(base, j, 0);
+      if (vec && i0 + 4 <= P) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(s + i0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[4 * j + e] = order_key(x[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[4 * j + e] = (i0 + e < P) ? order_key(s[i0 + e]) : 0u;
+      }
+    }
+  };
+
+  // ---- pass 0: load (and cache) the keys, find their range
+  if (tid == 0) {
+    sh[20] = 0xffffffffu;
+    sh[21] = 0u;
+  }
+  __syncthreads();
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int base = 0; base < P; base += kRound) {
+    uint32_t u[kPerThread];
+    load_round(base, u);
+#pragma unroll
+    for (int j = 0; j < kPerThread / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = elem(base, j, e);
+        if (i < P) {
+          if (cached) cache[i + (i >> 5)] = u[4 * j + e];
+          kmin = min(kmin, u[4 * j + e]);
+          kmax = max(kmax, u[4 * j + e]);
+        }
+      }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if ((tid & 63) == 0) {
+    atomicMin(&sh[20], kmin);
+    atomicMax(&sh[21], kmax);
+  }
+  __syncthreads();
+  kmin = sh[20];
+  kmax = sh[21];
+  const uint32_t range = kmax - kmin;
+  const int nbits = range == 0 ? 0 : 32 - __builtin_clz(range);
+
+  // ---- radix passes over x = key - kmin, 11 bits at a time from bit nbits down
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;  // x & pmask == prefix selects the live bucket
+  for (int hi = nbits; hi > 0;) {
+    const int lo = hi > 11 ? hi - 11 : 0;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
     if (tid == 0) {
       sh[18] = prefix;
       sh[19] = krem;
     }
     __syncthreads();
-    for (int i = tid; i < P; i += kTopkThreads) {
-      uint32_t u;
-      if (cached && shift != 24) {
-        u = cache[i];
+    for (int base = 0; base < P; base += kRound) {
+      uint32_t u[kPerThread];
+      if (cached) {
+        const int i0 = base + tid * kPerThread;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+          const int i = i0 + e;
+          const uint32_t x = (i < P ? cache[i + (i >> 5)] : kmin) - kmin;
+          if (i < P && (x & pmask) == prefix) atomicAdd(&hist[(x >> lo) & dmask], 1u);
+        }
       } else {
-        u = order_key(s[i]);
-        if (cached) cache[i] = u;
+        load_round(base, u);
+#pragma unroll
+        for (int j = 0; j < kPerThread / 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = u[4 * j + e] - kmin;
+            if (elem(base, j, e) < P && (x & pmask) == prefix) atomicAdd(&hist[(x >> lo) & dmask], 1u);
+          }
       }
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane 0 holds the top four bins, lane 63 the bottom four
-      uint32_t c[4], loc = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[e] = hist[255 - 4 * tid - e];
-        loc += c[e];
-      }
-      uint32_t inc = loc;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (tid >= o) inc += y;
-      }
-      const uint32_t exc = inc - loc;
-      if (exc < krem && krem <= inc) {
-        uint32_t cum = exc;
-        int bucket = 0;
-        uint32_t above = 0;
-        for (int e = 0; e < 4; ++e) {
-          if (cum + c[e] >= krem) {
-            bucket = 255 - 4 * tid - e;
-            above = cum;
-            break;
-          }
-          cum += c[e];
-        }
-        sh[18] = prefix | ((uint32_t)bucket << shift);
+    {
+      // suffix scan over the bins: thread t holds bins kBins-1-2t and kBins-2-2t
+      const uint32_t c0 = hist[kBins - 1 - 2 * tid], c1 = hist[kBins - 2 - 2 * tid];
+      uint32_t tot;
+      const uint32_t exc = block_excl_scan(c0 + c1, sh, &tot);
+      if (exc < krem && krem <= exc + c0 + c1) {
+        const bool first = exc + c0 >= krem;
+        const uint32_t bucket = first ? (uint32_t)(kBins - 1 - 2 * tid) : (uint32_t)(kBins - 2 - 2 * tid);
+        const uint32_t above = first ? exc : exc + c0;
+        sh[18] = prefix | (bucket << lo);
         sh[19] = krem - above;
       }
     }
     __syncthreads();
     prefix = sh[18];
     krem = sh[19];
-    pmask |= 255u << shift;
+    pmask |= dmask << lo;
     __syncthreads();
+    hi = lo;
   }
-  const uint32_t tau = prefix;  // key of the k-th largest score
-  const uint32_t need_eq = krem;  // entries equal to tau to keep, lowest index first
+  const uint32_t tau = prefix + kmin;  // key of the k-th largest score
+  const uint32_t need_eq = krem;       // entries equal to tau to keep, lowest index first
 
-  constexpr int E = 8;
+  // ---- emit in increasing index order: thread t owns indices [base + 32 t, base + 32 t + 32)
   uint32_t eq_carry = 0, sel_carry = 0;
-  for (int base = 0; base < P; base += kTopkThreads * E) {
-    const int i0 = base + tid * E;
-    uint32_t u[E];
+  for (int base = 0; base < P; base += kRound) {
+    const int i0 = base + tid * kPerThread;
+    uint32_t u[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e;
+      u[e] = i < P ? (cached ? cache[i + (i >> 5)] : order_key(s[i])) : 0u;
+    }
     uint32_t n_eq = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = i0 + e;
-      u[e] = (i < P) ? (cached ? cache[i] : order_key(s[i])) : 0u;
-      n_eq += (i < P && u[e] == tau) ? 1u : 0u;
-    }
+    for (int e = 0; e < kPerThread; ++e) n_eq += (i0 + e < P && u[e] == tau) ? 1u : 0u;
     uint32_t tot;
     uint32_t eq_before = eq_carry + block_excl_scan(n_eq, sh, &tot);
     eq_carry += tot;
     uint32_t selmask = 0, n_sel = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = i0 + e;
+    for (int e = 0; e < kPerThread; ++e) {
       bool sel = false;
-      if (i < P) {
+      if (i0 + e < P) {
         if (u[e] > tau) {
           sel = true;
         } else if (u[e] == tau) {
@@ -170,7 +234,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
     uint32_t pos = sel_carry + block_excl_scan(n_sel, sh, &tot);
     sel_carry += tot;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
+    for (int e = 0; e < kPerThread; ++e)
       if ((selmask & (1u << e)) && pos < (uint32_t)k) out[pos++] = i0 + e;
   }
   for (int i = k + tid; i < k_max; i += kTopkThreads) out[i] = -1;

@@ -26,27 +26,53 @@
 #include "sv_device.h"
 #include "sv_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <type_traits>
 
 namespace sv {
 
+// LDS ring geometry.  K and V rows are stored unpadded; 16-byte chunks of a
+// row are permuted by an XOR swizzle so that the MFMA operand reads (16-byte
+// K reads, 8-byte transpose reads of V) spread over all LDS banks, while every
+// global->LDS copy instruction still reads whole rows (four 256-byte rows per
+// 1 KB wave instruction for bf16, D = 128).
 template <typename T, int D>
-struct Tile {
+struct Ring {
   static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int TK = (!kBf16 && D == 128) ? 64 : 128;  // keys per LDS tile
-  static constexpr int NB = TK / 32;                         // 32-key blocks per tile
-  // LDS row strides (elements), chosen so the MFMA operand reads hit distinct banks.
-  static constexpr int KSTR = kBf16 ? (D == 128 ? 136 : 72) : (D == 128 ? 132 : 68);
-  static constexpr int VSTR = kBf16 ? (D == 128 ? 160 : 96) : (D == 128 ? 136 : 72);
   static constexpr int ROWB = D * (int)sizeof(T);  // bytes of one head's K (or V) row
   static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
-  static constexpr int LOADS = TK * CPR / 256;     // 16-byte loads per thread per tensor
-  static constexpr int KS_BYTES = TK * KSTR * (int)sizeof(T);
-  static constexpr int VS_BYTES = TK * VSTR * (int)sizeof(T);
-  static constexpr int EPI_BYTES = 4 * 32 * (D + 1) * 4 + 4 * 32 * 2 * 4;
-  static constexpr int LDS_BYTES = (KS_BYTES + VS_BYTES) > EPI_BYTES ? (KS_BYTES + VS_BYTES) : EPI_BYTES;
+  static constexpr int SK = ROWB > 256 ? 32 : 64;  // keys per stage
+  static constexpr int NB = SK / 32;               // 32-key MFMA blocks per stage
+  static constexpr int TILE = SK * ROWB;           // bytes of K (or V) per stage
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int NS = 4;                     // stages in the ring
+  static constexpr int PD = NS - 1;                // stages in flight ahead of compute
+  static constexpr int SEGS = STAGE / 1024;        // 1 KB copy instructions per stage
+  static constexpr int LPW = SEGS / 4;             // ... per wave
+  static constexpr int RPS = 1024 / ROWB;          // rows per copy instruction
+  static constexpr int RING = NS * STAGE;
+  static constexpr int EPI = 4 * 32 * (D + 1) * 4 + 4 * 32 * 2 * 4;
+  static constexpr int MAIN = RING > EPI ? RING : EPI;
+  static constexpr int PT_CAP = 1024;              // cached page-table entries per chunk
+  static constexpr int AUX_FLOATS = 512;           // qbar scratch
+  static constexpr int QBT = 3 * D * (int)sizeof(T);  // score operand table: qbar hi/mid/lo (bf16) or qbar (f32)
+  static constexpr int LDS = MAIN + PT_CAP * 4 + AUX_FLOATS * 4 + QBT;
+  static_assert(LPW * 4 == SEGS && RPS * ROWB == 1024, "ring geometry");
 };
+
+// chunk swizzle of row r (see Ring); the derivation per layout is in the design notes
+template <typename T, int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (sizeof(T) == 2 && D == 128) return ((r & 3) << 2) ^ ((r >> 2) & 3);
+  else if constexpr (sizeof(T) == 2) return (((r >> 1) & 1) << 2) ^ ((r >> 2) & 3);
+  else return (r & 7) ^ (((r >> 2) & 1) << 3);
+}
+template <typename T, int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * Ring<T, D>::ROWB + ((c ^ swz<T, D>(r)) << 4);
+}
 
 struct VerifyArgs {
   const void* q;
@@ -62,6 +88,7 @@ struct VerifyArgs {
   float* scores;
   int B, N, Hq, Hkv, G, R, RB, Rpad, P_max, chunk, n_chunks, n_units;
   int tree, do_scores, prep_qbar;
+  int ps_shift;  // log2(page_size) if it is a power of two, else -1
   float scale, scale_log2;
   int n_score_rows;
   uint16_t score_rows[kMaxNodes];
@@ -70,15 +97,25 @@ struct VerifyArgs {
 // key offset (within a 32-key block) of accumulator element v for lane half h
 __device__ __forceinline__ int kappa(int v, int h) { return mfma_row(v, h); }
 
-template <typename T, int D, int RT, int WR>
+// 2-lane-shifted copies within a row of 16 lanes (DPP): lane i gets lane i + N's x (0 past the row end)
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x100 + N, 0xf, 0xf, true));
+}
+
+template <typename T, int D, int RT, int WR, bool PAGED>
 __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
-  using TL = Tile<T, D>;
+  using RG = Ring<T, D>;
   constexpr int WK = 4 / WR;
-  constexpr bool kBf16 = TL::kBf16;
+  constexpr bool kBf16 = RG::kBf16;
   constexpr int DB = D / 32;  // 32-wide column blocks of the head dim
-  __shared__ __attribute__((aligned(16))) char smem[TL::LDS_BYTES];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = reinterpret_cast<T*>(smem + TL::KS_BYTES);
+  constexpr int QN = kBf16 ? D / 16 : D / 2;
+  constexpr int KRD = kBf16 ? D / 16 : D / 8;  // 16-byte K reads per 32-key block
+  __shared__ __attribute__((aligned(1024))) char smem[RG::LDS];
+  char* ring = smem;
+  int* pt_lds = reinterpret_cast<int*>(smem + RG::MAIN);
+  float* qs = reinterpret_cast<float*>(smem + RG::MAIN + RG::PT_CAP * 4);
+  T* qbt = reinterpret_cast<T*>(smem + RG::MAIN + RG::PT_CAP * 4 + RG::AUX_FLOATS * 4);
 
   // ---- workgroup -> (sequence, KV head, chunk, row block); consecutive logical
   // ids (same head, neighbouring chunks, all row blocks) land on one XCD.
@@ -103,41 +140,96 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   const int wave = tid >> 6, lane = tid & 63, lane32 = lane & 31, h = lane >> 5;
   const int wk = wave % WK, wr = wave / WK;
 
+  // ---- page-table slice of this chunk -> LDS
+  const int ps = a.kv.page_size;
+  int pg0 = 0;
+  if constexpr (PAGED) {
+    pg0 = a.ps_shift >= 0 ? (c0 >> a.ps_shift) : c0 / ps;
+    const int pg1 = a.ps_shift >= 0 ? ((c1 - 1) >> a.ps_shift) : (c1 - 1) / ps;
+    for (int j = tid; j <= pg1 - pg0 && j < RG::PT_CAP; j += 256) {
+      const int pg = pg0 + j;
+      pt_lds[j] = pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1;
+    }
+    __syncthreads();
+  }
+  const long long seq_base = (long long)b * a.kv.seq_stride;
+  auto slot_of = [&](int pos) -> long long {
+    long long s;
+    if constexpr (PAGED) {
+      const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
+      const int e = pt_lds[pg - pg0];  // the plan keeps every chunk within PT_CAP pages
+      s = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
+    } else {
+      s = seq_base + pos;
+    }
+    return (s >= 0 && s < a.kv.num_slots) ? s : 0;  // unmapped positions read slot 0 (never visible)
+  };
+
+  // ---- global -> LDS copies of one stage.  A wave's LPW copies all go to the
+  // same tensor (waves 0..1 fill K, 2..3 fill V); each lane's row and swizzled
+  // column within the stage are the same for every stage, so they are set once.
+  const bool wave_v = wave * RG::LPW >= RG::SEGS / 2;
+  const char* tbase = reinterpret_cast<const char*>(wave_v ? a.kv.v : a.kv.k) + (long long)g * RG::ROWB;
+  const long long slot_bytes = (long long)a.Hkv * RG::ROWB;
+  int dma_row[RG::LPW], dma_off[RG::LPW];
+#pragma unroll
+  for (int j = 0; j < RG::LPW; ++j) {
+    const int sgt = (wave * RG::LPW + j) % (RG::SEGS / 2);
+    dma_row[j] = sgt * RG::RPS + lane / RG::CPR;
+    const int cl = (lane % RG::CPR) ^ swz<T, D>(dma_row[j]);
+    dma_off[j] = (int)(dma_row[j] * slot_bytes) + cl * 16;
+  }
+  const int n_st = (c1 - c0 + RG::SK - 1) / RG::SK;
+  auto issue = [&](int i) {
+    const int key0 = c0 + i * RG::SK;
+    char* dst = ring + (i % RG::NS) * RG::STAGE + wave * RG::LPW * 1024;
+    if (!PAGED && key0 + RG::SK <= c1 && seq_base + key0 + RG::SK <= a.kv.num_slots) {
+      const char* base = tbase + (seq_base + key0) * slot_bytes;  // wave-uniform
+#pragma unroll
+      for (int j = 0; j < RG::LPW; ++j) global_to_lds16(base + dma_off[j], dst + j * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < RG::LPW; ++j) {
+        const int pos = key0 + dma_row[j];
+        const long long sl = pos < c1 ? slot_of(pos) : slot_of(c0);
+        global_to_lds16(tbase + sl * slot_bytes + (dma_off[j] - (int)(dma_row[j] * slot_bytes)), dst + j * 1024);
+      }
+    }
+  };
+  for (int i = 0; i < RG::PD && i < n_st; ++i) issue(i);
+
   // ---- query fragments (B operand of S^T = K Q^T): lane column = query row
   typedef typename std::conditional<kBf16, bf16x8, float>::type QElem;
-  constexpr int QN = kBf16 ? D / 16 : D / 2;
   QElem qf[RT][QN];
   int row_node[RT];
-  bool row_ok[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = ((rb * WR + wr) * RT + rt) * 32 + lane32;
-    row_ok[rt] = r < a.R;
-    const int t = row_ok[rt] ? r / a.G : a.N - 1;
+    const bool ok = r < a.R;
+    const int t = ok ? r / a.G : a.N - 1;
     row_node[rt] = t;
-    const int j = row_ok[rt] ? r % a.G : 0;
+    const int j = ok ? r % a.G : 0;
     const T* qrow = reinterpret_cast<const T*>(a.q) + ((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D;
     if constexpr (kBf16) {
 #pragma unroll
       for (int ks = 0; ks < QN; ++ks) {
         bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * h);
-        qf[rt][ks] = row_ok[rt] ? x : bf16x8{};
+        qf[rt][ks] = ok ? x : bf16x8{};
       }
     } else {
 #pragma unroll
       for (int cc = 0; cc < D / 8; ++cc) {
         f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 8 * cc + 4 * h);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qf[rt][4 * cc + e] = row_ok[rt] ? x[e] : 0.f;
+        for (int e = 0; e < 4; ++e) qf[rt][4 * cc + e] = ok ? x[e] : 0.f;
       }
     }
   }
 
-  // ---- score operand: qbar_g split into bf16 hi/mid/lo in MFMA columns 0..2
+  // ---- score operand: qbar_g (fp32) split into bf16 hi + mid + lo, kept in
+  // LDS as three rows; they become MFMA columns 0..2 of S^T's companion tile
   const bool wg_scores = a.do_scores && rb == 0 && c0 < Pb;
-  QElem qb[QN];
   if (wg_scores) {
-    float* qs = reinterpret_cast<float*>(smem);
     if (a.prep_qbar) {
       for (int d = tid; d < D; d += 256) qs[d] = a.ws_qbar[(b * a.Hkv + g) * D + d];
     } else {
@@ -153,46 +245,62 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
       qs[D + part * D + d] = acc;
       __syncthreads();
       if (tid < D) {
-        float s = 0.f;
-        for (int p = 0; p < NP; ++p) s += qs[D + p * D + tid];
-        qs[tid] = s;
+        float sacc = 0.f;
+        for (int p = 0; p < NP; ++p) sacc += qs[D + p * D + tid];
+        qs[tid] = sacc;
       }
     }
     __syncthreads();
-    if constexpr (kBf16) {
-#pragma unroll
-      for (int ks = 0; ks < QN; ++ks) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = qs[16 * ks + 8 * h + e];
-          const bf16 hi = (bf16)x;
-          const float r1 = x - (float)hi;
-          const bf16 mid = (bf16)r1;
-          const float r2 = r1 - (float)mid;
-          const bf16 lo = (bf16)r2;
-          v[e] = lane32 == 0 ? hi : (lane32 == 1 ? mid : (lane32 == 2 ? lo : (bf16)0.f));
-        }
-        qb[ks] = v;
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < QN; ++kk) {
-        const int d = 8 * (kk >> 2) + 4 * h + (kk & 3);
-        qb[kk] = lane32 == 0 ? qs[d] : 0.f;
+    for (int d = tid; d < D; d += 256) {
+      const float x = qs[d];
+      if constexpr (kBf16) {
+        const bf16 hi = (bf16)x;
+        const float r1 = x - (float)hi;
+        const bf16 mid = (bf16)r1;
+        const bf16 lo = (bf16)(r1 - (float)mid);
+        qbt[d] = hi;
+        qbt[D + d] = mid;
+        qbt[2 * D + d] = lo;
+      } else {
+        qbt[d] = x;
       }
     }
     __syncthreads();
   }
+  // B-operand fragment of the score tile for k-step ks (nonzero only in lanes of columns 0..2)
+  auto qb_frag = [&](int ks) -> QElem {
+    if constexpr (kBf16) {
+      bf16x8 v = bf16x8{};
+      if (lane32 < 3) v = *reinterpret_cast<const bf16x8*>(qbt + lane32 * D + 16 * ks + 8 * h);
+      return v;
+    } else {
+      const int d = 8 * (ks >> 2) + 4 * h + (ks & 3);
+      return lane32 == 0 ? qbt[d] : 0.f;
+    }
+  };
 
   // ---- ancestor bitsets of this lane's rows (tree, chunk reaching the verify tokens)
   uint32_t anc[RT][kAncWords];
-  const bool has_tail = c1 > Pb;
-  if (a.tree && has_tail) {
+  if (a.tree && c1 > Pb) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int w = 0; w < kAncWords; ++w) anc[rt][w] = a.ws_anc[((long long)b * a.N + row_node[rt]) * kAncWords + w];
+  }
+
+  // ---- per-lane LDS offsets of the MFMA operand reads inside a 32-key block;
+  // the swizzle depends on row & 15 only, so blocks and stages just add a base
+  int koff[KRD];
+#pragma unroll
+  for (int kr = 0; kr < KRD; ++kr) koff[kr] = tile_off<T, D>(lane32, 2 * kr + h);
+  const int e4 = (lane & 15) >> 2, cq = lane & 3, dh = (lane >> 4) & 1;
+  int voff[kBf16 ? DB : 1][2];
+  if constexpr (kBf16) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+        voff[db][hl] = tile_off<T, D>(4 * h + e4 + 8 * hl, 4 * db + 2 * dh + (cq >> 1)) + (cq & 1) * 8;
   }
 
   // ---- running softmax state
@@ -206,83 +314,74 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
     for (int db = 0; db < DB; ++db) o[rt][db] = f32x16{};
   }
 
-  // ---- tile pipeline: registers hold tile it+1 while LDS holds tile it
-  const char* kbase = reinterpret_cast<const char*>(a.kv.k) + (long long)g * TL::ROWB;
-  const char* vbase = reinterpret_cast<const char*>(a.kv.v) + (long long)g * TL::ROWB;
-  const long long slot_bytes = (long long)a.Hkv * TL::ROWB;
-  uint4 kr[TL::LOADS], vr[TL::LOADS];
-  auto load_tile = [&](int ts) {
-#pragma unroll
-    for (int i = 0; i < TL::LOADS; ++i) {
-      const int ci = tid + 256 * i, key = ci / TL::CPR, col = ci % TL::CPR;
-      const int pos = ts + key;
-      long long s = pos < c1 ? a.kv.slot(b, pos) : -1;
-      if (s >= 0) {
-        kr[i] = *reinterpret_cast<const uint4*>(kbase + s * slot_bytes + col * 16);
-        vr[i] = *reinterpret_cast<const uint4*>(vbase + s * slot_bytes + col * 16);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < TL::LOADS; ++i) {
-      const int ci = tid + 256 * i, key = ci / TL::CPR, col = ci % TL::CPR;
-      *reinterpret_cast<uint4*>(smem + key * TL::KSTR * (int)sizeof(T) + col * 16) = kr[i];
-      *reinterpret_cast<uint4*>(smem + TL::KS_BYTES + key * TL::VSTR * (int)sizeof(T) + col * 16) = vr[i];
-    }
-  };
+  for (int i = 0; i < n_st; ++i) {
+    // stage i has landed once at most (stages issued after it) x LPW copies are outstanding
+    const int after = min(RG::PD - 1, n_st - 1 - i);
+    if (after >= 2) wait_vm_lgkm0<2 * RG::LPW>();
+    else if (after == 1) wait_vm_lgkm0<RG::LPW>();
+    else wait_vm_lgkm0<0>();
+    barrier_only();
+    // the buffer of stage i + PD was last read in iteration i - 1, which every wave has finished
+    if (i + RG::PD < n_st) issue(i + RG::PD);
 
-  const int n_tiles = (c1 - c0 + TL::TK - 1) / TL::TK;
-  load_tile(c0);
-  for (int it = 0; it < n_tiles; ++it) {
-    const int ts = c0 + it * TL::TK;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile(ts + TL::TK);
-
-    for (int kb = wk; kb < TL::NB; kb += WK) {
-      const int kb0 = ts + 32 * kb;
+    const char* Kt = ring + (i % RG::NS) * RG::STAGE;
+    const char* Vt = Kt + RG::TILE;
+#pragma unroll
+    for (int kb = 0; kb < RG::NB; ++kb) {
+      const int gb = i * RG::NB + kb;
+      if ((gb % WK) != wk) continue;
+      const int kb0 = c0 + 32 * gb;
       if (kb0 >= c1) break;
-      const bool do_score = wg_scores && kb0 < Pb && ((kb / WK) % WR) == wr;
-      f32x16 s[RT];
+      const bool do_score = wg_scores && kb0 < Pb && ((gb / WK) % WR) == wr;
+      const char* Kb = Kt + kb * 32 * RG::ROWB;
+      const char* Vb = Vt + kb * 32 * RG::ROWB;
+
+      // S^T = K Q^T in two independent accumulation chains (and the score columns)
+      f32x16 s[RT], s2[RT];
       f32x16 sc = f32x16{};
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) s[rt] = f32x16{};
-
-      // S^T = K Q^T (and the score columns)
-      const T* krow = Ks + (32 * kb + lane32) * TL::KSTR;
+      for (int rt = 0; rt < RT; ++rt) {
+        s[rt] = f32x16{};
+        s2[rt] = f32x16{};
+      }
       if constexpr (kBf16) {
+        bf16x8 ka[QN];
+#pragma unroll
+        for (int ks = 0; ks < QN; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(Kb + koff[ks]);
 #pragma unroll
         for (int ks = 0; ks < QN; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ks + 8 * h);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) s[rt] = mfma_bf16(ka, qf[rt][ks], s[rt]);
-          if (do_score) sc = mfma_bf16(ka, qb[ks], sc);
+          for (int rt = 0; rt < RT; ++rt) {
+            if (ks & 1) s2[rt] = mfma_bf16(ka[ks], qf[rt][ks], s2[rt]);
+            else s[rt] = mfma_bf16(ka[ks], qf[rt][ks], s[rt]);
+          }
+          if (do_score) sc = mfma_bf16(ka[ks], qb_frag(ks), sc);
         }
       } else {
 #pragma unroll
         for (int cc = 0; cc < D / 8; ++cc) {
-          const f32x4 ka = *reinterpret_cast<const f32x4*>(krow + 8 * cc + 4 * h);
+          const f32x4 ka = *reinterpret_cast<const f32x4*>(Kb + koff[cc]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) s[rt] = mfma_f32(ka[e], qf[rt][4 * cc + e], s[rt]);
-            if (do_score) sc = mfma_f32(ka[e], qb[4 * cc + e], sc);
+            for (int rt = 0; rt < RT; ++rt) {
+              if (e & 1) s2[rt] = mfma_f32(ka[e], qf[rt][4 * cc + e], s2[rt]);
+              else s[rt] = mfma_f32(ka[e], qf[rt][4 * cc + e], s[rt]);
+            }
+            if (do_score) sc = mfma_f32(ka[e], qb_frag(4 * cc + e), sc);
           }
         }
       }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) s[rt] += s2[rt];
 
       if (do_score) {
-        // column sum hi + mid + lo (lanes 0..2 / 32..34), written by lanes 0 and 32
+        // column sum hi + mid + lo (lanes 0..2 / 32..34 of their 16-lane rows), written by lanes 0 and 32
         float tv[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float x = sc[v];
-          if constexpr (kBf16) x = x + __shfl_down(sc[v], 1) + __shfl_down(sc[v], 2);
+          if constexpr (kBf16) x = x + row_shl<1>(sc[v]) + row_shl<2>(sc[v]);
           tv[v] = x * a.scale;
         }
         if (lane32 == 0) {
@@ -327,7 +426,7 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
         }
       }
 
-      // online softmax (log2 domain)
+      // online softmax (log2 domain); the O rescale is skipped when no row's max moved
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float mx = kNegInf;
@@ -337,25 +436,28 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
           mx = fmaxf(mx, s[rt][v]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m[rt], mx);
+        const bool grew = mx > m[rt];
+        const float mn = grew ? mx : m[rt];
         const bool live = mn != kNegInf;
-        const float alpha = live ? fast_exp2(m[rt] - mn) : 1.f;
-        float ps = 0.f;
+        float psum = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = live ? fast_exp2(s[rt][v] - mn) : 0.f;
           s[rt][v] = p;
-          ps += p;
+          psum += p;
         }
-        l[rt] = l[rt] * alpha + ps;
-        m[rt] = mn;
+        if (__any(grew)) {
+          const float alpha = grew ? fast_exp2(m[rt] - mn) : 1.f;
+          l[rt] *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[rt][db] *= alpha;
+          for (int db = 0; db < DB; ++db) o[rt][db] *= alpha;
+        }
+        l[rt] += psum;
+        m[rt] = mn;
       }
 
       // O^T += V^T P^T
       if constexpr (kBf16) {
-        const int e = (lane & 15) >> 2, cq = lane & 3, dh = (lane >> 4) & 1;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           bf16x8 pb[RT];
@@ -363,11 +465,11 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int u = 0; u < 8; ++u) pb[rt][u] = (bf16)s[rt][8 * jj + u];
-          const T* v0 = Vs + (32 * kb + 16 * jj + 4 * h + e) * TL::VSTR + 16 * dh + 4 * cq;
+          const char* Vj = Vb + jj * 16 * RG::ROWB;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x4 lo = lds_read_tr16(v0 + 32 * db);
-            const bf16x4 hi = lds_read_tr16(v0 + 8 * TL::VSTR + 32 * db);
+            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const T*>(Vj + voff[db][0]));
+            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const T*>(Vj + voff[db][1]));
             const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) o[rt][db] = mfma_bf16(va, pb[rt], o[rt][db]);
@@ -376,10 +478,11 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const T* vrow = Vs + (32 * kb + kappa(v, h)) * TL::VSTR + lane32;
+          const int vr = kappa(v, h);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const float va = vrow[32 * db];
+            const float va = *reinterpret_cast<const float*>(
+                Vb + tile_off<T, D>(vr, 8 * db + (lane32 >> 2)) + (lane32 & 3) * 4);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) o[rt][db] = mfma_f32(va, s[rt][v], o[rt][db]);
           }
@@ -389,6 +492,7 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   }
 
   // ---- epilogue: combine the WK waves that share rows, write (m, l, o) partials
+  wait_vm_lgkm0<0>();
   constexpr int OS = D + 1;
   float* lo_ = reinterpret_cast<float*>(smem);            // [4 waves][32 rows][D+1]
   float* lml = lo_ + 4 * 32 * OS;                          // [4 waves][32 rows][2]
@@ -428,36 +532,67 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   }
 }
 
-// Split-KV merge (log-sum-exp weights) + per-KV-head score sum.
+__device__ __forceinline__ float block_reduce_max(float x, float* red) {
+  x = wave_max(x);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_reduce_sum(float x, float* red) {
+  x = wave_sum(x);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Split-KV merge (log-sum-exp weights) + per-KV-head score sum.  One
+// workgroup per (sequence, KV head, query row): all chunk partials of the row
+// are read at once, spread over the threads, and reduced in a fixed order.
+constexpr int kMaxChunks = 1024;
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_row_wgs) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < n_row_wgs) {
-    const int wave = tid >> 6, lane = tid & 63;
-    const int gr = blockIdx.x * 4 + wave;  // (b, g, row)
-    if (gr >= a.B * a.Hkv * a.R) return;
+    __shared__ float wsh[kMaxChunks];
+    __shared__ float red[4];
+    __shared__ f32x4 part[256];
+    const int gr = blockIdx.x;  // (b, g, row)
     const int row = gr % a.R, bg = gr / a.R, g = bg % a.Hkv, b = bg / a.Hkv;
     int Pb = a.prefix_len[b];
     Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
     const int nc = min((Pb + a.N + a.chunk - 1) / a.chunk, a.n_chunks);
     const long long rec0 = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks;
-    float M = kNegInf;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, a.ws_ml[rec0 + c][0]);
-    constexpr int PER = D / 64;
-    float acc[PER] = {};
-    float lsum = 0.f;
-    for (int c = 0; c < nc; ++c) {
+    float mloc = kNegInf;
+    for (int c = tid; c < nc; c += 256) mloc = fmaxf(mloc, a.ws_ml[rec0 + c][0]);
+    const float M = block_reduce_max(mloc, red);
+    float lloc = 0.f;
+    for (int c = tid; c < nc; c += 256) {
       const f32x2 ml = a.ws_ml[rec0 + c];
-      const float wt = (M == kNegInf) ? 0.f : fast_exp2(ml[0] - M);
-      lsum += wt * ml[1];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += wt * a.ws_o[(rec0 + c) * D + lane * PER + e];
+      const float w = (M == kNegInf) ? 0.f : fast_exp2(ml[0] - M);
+      wsh[c] = w;
+      lloc += w * ml[1];
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int t = row / a.G, j = row % a.G;
-    T* dst = reinterpret_cast<T*>(a.out) + ((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + lane * PER;
+    const float lsum = block_reduce_sum(lloc, red);  // (its barriers also publish wsh)
+    constexpr int Q4 = D / 4, PH = 256 / Q4;
+    const int quad = tid % Q4, ph = tid / Q4;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int c = ph; c < nc; c += PH)
+      acc += wsh[c] * *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * quad);
+    part[tid] = acc;
+    __syncthreads();
+    if (tid < Q4) {
+      f32x4 t = part[tid];
+      for (int p2 = 1; p2 < PH; ++p2) t += part[p2 * Q4 + tid];
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const int tn = row / a.G, j = row % a.G;
+      T* dst = reinterpret_cast<T*>(a.out) + ((long long)(b * a.N + tn) * a.Hq + g * a.G + j) * D + 4 * tid;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = (T)(acc[e] * inv);
+      for (int e = 0; e < 4; ++e) dst[e] = (T)(t[e] * inv);
+    }
   } else {
     const long long i0 = (long long)(blockIdx.x - n_row_wgs) * 256 + tid;
     if (i0 >= (long long)a.B * a.P_max) return;
@@ -466,6 +601,7 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
     Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
     if (i >= Pb) return;
     float s = 0.f;
+#pragma unroll 8
     for (int g = 0; g < a.Hkv; ++g) s += a.ws_s[((long long)b * a.Hkv + g) * a.P_max + i];
     a.scores[i0] = s;
   }
@@ -535,7 +671,7 @@ __global__ void __launch_bounds__(256) verify_prep(const VerifyArgs a, int n_qba
 // ------------------------------------------------------------------------- host side
 
 VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtype, bool tree,
-                       int n_score_rows) {
+                       int n_score_rows, int page_size) {
   VerifyPlan p{};
   p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.D = D; p.P_max = P_max; p.dtype = dtype;
   p.R = N * p.G;
@@ -548,15 +684,24 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   p.rows_per_block = p.RT * p.WR * 32;
   p.RB = (p.R + p.rows_per_block - 1) / p.rows_per_block;
   p.Rpad = p.RB * p.rows_per_block;
-  p.TK = (dtype == SV_F32 && D == 128) ? 64 : 128;
+  const int es = dtype == SV_BF16 ? 2 : 4;
+  const int SK = D * es > 256 ? 32 : 64;  // keys per ring stage (Ring<T, D>::SK)
+  p.TK = SK;
+  // one resident workgroup per CU (two for the smaller bf16, D = 64 ring)
+  const int occ = (dtype == SV_BF16 && D == 64) ? 2 : 1;
   const long long Lmax = (long long)P_max + N;
   const long long units = (long long)B * Hkv * p.RB;
-  const long long target = 512;  // about two resident workgroups per CU
-  long long want = (target + units - 1) / units;
+  const long long target = 256LL * occ;
+  long long want = (target + units / 2) / units;
   if (want < 1) want = 1;
-  long long chunk = (Lmax + want - 1) / want;
-  chunk = (chunk + 31) / 32 * 32;
-  if (chunk < 32) chunk = 32;
+  long long chunk = Lmax / want / SK * SK;
+  if (chunk < SK) chunk = SK;
+  if (chunk > 16320) chunk = 16320;
+  if ((Lmax + chunk - 1) / chunk > kMaxChunks) chunk = ((Lmax + kMaxChunks - 1) / kMaxChunks + SK - 1) / SK * SK;
+  if (page_size > 0) {  // a chunk's page-table slice must fit the LDS copy (Ring::PT_CAP entries)
+    const long long cap = (long long)(Ring<float, 64>::PT_CAP - 2) * page_size / SK * SK;
+    if (chunk > cap) chunk = cap < SK ? SK : cap;
+  }
   p.chunk = (int)chunk;
   p.n_chunks = (int)((Lmax + chunk - 1) / chunk);
   long long n_units = units * p.n_chunks;
@@ -575,9 +720,18 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   return p;
 }
 
+template <typename T, int D, int RT, int WR, bool PAGED>
+static void launch_main2(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
+  if (ev0 && ev1)  // timestamps taken by the dispatch itself: no extra marker packets in the stream
+    hipExtLaunchKernelGGL((verify_main<T, D, RT, WR, PAGED>), dim3(p.n_wg), dim3(256), 0, st, (hipEvent_t)ev0,
+                          (hipEvent_t)ev1, 0, a);
+  else
+    hipLaunchKernelGGL((verify_main<T, D, RT, WR, PAGED>), dim3(p.n_wg), dim3(256), 0, st, a);
+}
 template <typename T, int D, int RT, int WR>
-static void launch_main(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((verify_main<T, D, RT, WR>), dim3(p.n_wg), dim3(256), 0, st, a);
+static void launch_main(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
+  if (a.kv.page_table) launch_main2<T, D, RT, WR, true>(p, a, st, ev0, ev1);
+  else launch_main2<T, D, RT, WR, false>(p, a, st, ev0, ev1);
 }
 
 template <typename T, int D>
@@ -587,13 +741,11 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
     const int nt = p.tree ? p.B : 0;
     hipLaunchKernelGGL((verify_prep<T, D>), dim3(nq + nt), dim3(256), 0, st, a, nq);
   }
-  if (ev0) (void)hipEventRecord((hipEvent_t)ev0, st);
-  if (p.RT == 1 && p.WR == 1) launch_main<T, D, 1, 1>(p, a, st);
-  else if (p.RT == 2 && p.WR == 1) launch_main<T, D, 2, 1>(p, a, st);
-  else if (p.RT == 2 && p.WR == 2) launch_main<T, D, 2, 2>(p, a, st);
-  else launch_main<T, D, 2, 4>(p, a, st);
-  if (ev1) (void)hipEventRecord((hipEvent_t)ev1, st);
-  const int n_row_wgs = (p.B * p.Hkv * p.R + 3) / 4;
+  if (p.RT == 1 && p.WR == 1) launch_main<T, D, 1, 1>(p, a, st, ev0, ev1);
+  else if (p.RT == 2 && p.WR == 1) launch_main<T, D, 2, 1>(p, a, st, ev0, ev1);
+  else if (p.RT == 2 && p.WR == 2) launch_main<T, D, 2, 2>(p, a, st, ev0, ev1);
+  else launch_main<T, D, 2, 4>(p, a, st, ev0, ev1);
+  const int n_row_wgs = p.B * p.Hkv * p.R;
   const long long n_s = p.scores ? ((long long)p.B * p.P_max + 255) / 256 : 0;
   hipLaunchKernelGGL((verify_merge<T, D>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs);
   return (int)hipGetLastError();
@@ -618,6 +770,11 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
   a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.R = p.R; a.RB = p.RB; a.Rpad = p.Rpad;
   a.P_max = p.P_max; a.chunk = p.chunk; a.n_chunks = p.n_chunks;
   a.n_units = p.B * p.Hkv * p.RB * p.n_chunks;
+  a.ps_shift = -1;
+  if (kv.page_table && kv.page_size > 0 && (kv.page_size & (kv.page_size - 1)) == 0) {
+    a.ps_shift = 0;
+    while ((1 << a.ps_shift) < kv.page_size) ++a.ps_shift;
+  }
   a.tree = p.tree; a.do_scores = p.scores; a.prep_qbar = p.prep_qbar;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
