@@ -30,6 +30,10 @@ def flags() -> list[str]:
         "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
         # keep the compiler from emitting packed fp32 arithmetic
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs: the attention loops rescale their
+        # accumulators with vector ALU ops, and the AGPR form made the compiler
+        # copy them between register files on every iteration
+        "-mllvm", "-amdgpu-mfma-vgpr-form=true",
         "-I", INCLUDE, "-I", CSRC,
         "-Wall", "-Wno-unused-function", "-Wno-unused-result",
     ]

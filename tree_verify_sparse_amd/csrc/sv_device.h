@@ -68,6 +68,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
+
 // Workgroup barrier without the memory fence __syncthreads() implies (the
 // fence would make the compiler drain every outstanding global->LDS copy).
 // Callers order memory explicitly with wait_vm_lgkm0 first.

@@ -26,6 +26,7 @@ struct VerifyPlan {
   int n_chunks;     // splits covering the longest sequence (P_max + N)
   int n_wg;         // workgroups of the main kernel (multiple of 8)
   bool tree, scores, prep_qbar, prep;
+  bool stream;      // bf16 with R <= 64: the key-split streaming kernel (verify_stream)
   size_t off_o, off_ml, off_s, off_qbar, off_anc, bytes;
 };
 

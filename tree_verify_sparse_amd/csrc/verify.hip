@@ -88,6 +88,7 @@ struct VerifyArgs {
   float* scores;
   int B, N, Hq, Hkv, G, R, RB, Rpad, P_max, chunk, n_chunks, n_units;
   int tree, do_scores, prep_qbar;
+  int all_chunks;  // every chunk writes a partial (streaming kernel), else only chunks below P_b + N
   int ps_shift;  // log2(page_size) if it is a power of two, else -1
   float scale, scale_log2;
   int n_score_rows;
@@ -280,7 +281,7 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   };
 
   // ---- ancestor bitsets of this lane's rows (tree, chunk reaching the verify tokens)
-  uint32_t anc[RT][kAncWords];
+  uint32_t anc[RT][kAncWords] = {};
   if (a.tree && c1 > Pb) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -403,26 +404,26 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
 
       // mask: keys past the chunk end, and verify tokens that are not ancestors-or-self
       if (kb0 + 32 > min(Pb, c1)) {
+        if (a.tree) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int t = row_node[rt];
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = kb0 + kappa(v, h);
-            bool vis = key < c1;
-            if (vis && key >= Pb) {
-              const int an = key - Pb;
-              if (a.tree) {
-                uint32_t word = 0;
+            for (int v = 0; v < 16; ++v) {
+              const int key = kb0 + kappa(v, h), an = key - Pb;
+              uint32_t word = 0;
 #pragma unroll
-                for (int w = 0; w < kAncWords; ++w) word = ((an >> 5) == w) ? anc[rt][w] : word;
-                vis = (word >> (an & 31)) & 1u;
-              } else {
-                vis = an <= t;
-              }
+              for (int w = 0; w < kAncWords; ++w) word = ((an >> 5) == w) ? anc[rt][w] : word;
+              const bool vis = key < c1 && (an < 0 || ((word >> (an & 31)) & 1u));
+              s[rt][v] = vis ? s[rt][v] : kNegInf;
             }
-            if (!vis) s[rt][v] = kNegInf;
-          }
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int key = kb0 + kappa(v, h);
+              s[rt][v] = (key < c1 && key - Pb <= row_node[rt]) ? s[rt][v] : kNegInf;
+            }
         }
       }
 
@@ -532,6 +533,457 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel for few query rows per KV head (bf16, N * G <= 64: chains
+// and small trees).  All rows of a KV head fit one or two 32-column MFMA
+// tiles, so the four waves of a workgroup split the keys instead of the rows:
+// each wave owns a contiguous run of 32-key blocks and a private LDS ring that
+// only it fills (global->LDS copies) and reads.  Nothing is shared between
+// waves until the epilogue, so the loop has no workgroup barrier and every
+// wave streams at its own pace.  Per block the wave computes S^T = K Q^T
+// (plus the score columns), the online softmax and O^T += V^T P^T exactly as
+// verify_main does.
+template <int D>
+struct WaveRing {
+  static constexpr int ROWB = D * 2;             // bytes of one head's bf16 row
+  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;        // rows per 1 KB copy instruction
+  static constexpr int TILE = 32 * ROWB;         // K (or V) bytes of a 32-key block
+  static constexpr int LPT = TILE / 1024;        // copy instructions per tile
+  static constexpr int BLK = 2 * TILE;           // K + V of a block
+  static constexpr int NSW = D == 128 ? 2 : 4;   // blocks in a wave's ring
+  static constexpr int WAVE = NSW * BLK;
+  static constexpr int RING = 4 * WAVE;
+  static constexpr int EPI = 4 * 32 * (D + 1) * 4 + 4 * 32 * 2 * 4;
+  static constexpr int MAIN = RING > EPI ? RING : EPI;
+  static constexpr int PT_CAP = 1024;            // cached page-table entries per chunk
+  static constexpr int AUX_FLOATS = 512;
+  static constexpr int QBT = 3 * D * 2;
+  static constexpr int LDS = MAIN + PT_CAP * 4 + AUX_FLOATS * 4 + QBT;
+  static_assert(LPT * 1024 == TILE && RPI * ROWB == 1024, "wave ring geometry");
+};
+
+// One 16-byte-per-lane global->LDS copy (1 KB per wave).  `lds` is the
+// wave-uniform LDS byte address, `off` a per-lane 32-bit offset from the
+// wave-uniform base `base` (the scalar-base form of the instruction).
+__device__ __forceinline__ void dma16_sbase(uint32_t lds, uint32_t off, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma16_vaddr(uint32_t lds, const void* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr) : "memory");
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in {0, step, 2 step, 3 step}
+template <int STEP>
+__device__ __forceinline__ void wait_blocks_after(int blocks) {
+  if (blocks >= 3) wait_vm_lgkm0<3 * STEP>();
+  else if (blocks == 2) wait_vm_lgkm0<2 * STEP>();
+  else if (blocks == 1) wait_vm_lgkm0<STEP>();
+  else wait_vm_lgkm0<0>();
+}
+
+// Combine lane l with lane l ^ 32.  v_permlane32_swap with both operands equal
+// returns {x of lanes 0-31 in both halves, x of lanes 32-63 in both halves}.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// Lazy rescale threshold (log2 units): the running max is only moved when a
+// block's max exceeds it by more than this, so p <= 2^8 and O is rescaled a
+// handful of times per chunk instead of per block.
+constexpr float kRescaleSlack = 8.f;
+
+template <int D, int RT, bool PAGED>
+__global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
+  using WRg = WaveRing<D>;
+  using T = bf16;
+  constexpr int DB = D / 32;
+  constexpr int QN = D / 16;
+  constexpr int STEP = 2 * WRg::LPT;  // copy instructions per block
+  __shared__ __attribute__((aligned(1024))) char smem[WRg::LDS];
+  int* pt_lds = reinterpret_cast<int*>(smem + WRg::MAIN);
+  float* qs = reinterpret_cast<float*>(smem + WRg::MAIN + WRg::PT_CAP * 4);
+  T* qbt = reinterpret_cast<T*>(smem + WRg::MAIN + WRg::PT_CAP * 4 + WRg::AUX_FLOATS * 4);
+
+  // ---- workgroup -> (sequence, KV head, chunk); neighbouring chunks share an XCD
+  const int per = gridDim.x >> 3;
+  const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lid >= a.n_units) return;
+  const int c = lid % a.n_chunks;
+  const int bg = lid / a.n_chunks;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  int Pb = a.prefix_len[b];
+  Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
+  const int L = Pb + a.N;
+  const int nbk = (L + 31) >> 5;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lane32 = lane & 31, h = lane >> 5;
+
+  // balanced split of the sequence's blocks over all waves of all its chunks
+  const long long WT = (long long)a.n_chunks * 4;
+  const int blk0 = (int)((long long)(c * 4 + wave) * nbk / WT);
+  const int blk1 = (int)((long long)(c * 4 + wave + 1) * nbk / WT);
+  const int cblk0 = (int)((long long)c * 4 * nbk / WT);
+  const int cblk1 = (int)((long long)(c * 4 + 4) * nbk / WT);
+
+  // ---- page-table slice of this chunk -> LDS
+  const int ps = a.kv.page_size;
+  int pg0 = 0;
+  if constexpr (PAGED) {
+    const int k0 = cblk0 * 32, k1 = min(cblk1 * 32, L);
+    if (k1 > k0) {
+      pg0 = a.ps_shift >= 0 ? (k0 >> a.ps_shift) : k0 / ps;
+      const int pg1 = a.ps_shift >= 0 ? ((k1 - 1) >> a.ps_shift) : (k1 - 1) / ps;
+      for (int j = tid; j <= pg1 - pg0 && j < WRg::PT_CAP; j += 256) {
+        const int pg = pg0 + j;
+        pt_lds[j] = pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1;
+      }
+    }
+    __syncthreads();
+  }
+  const long long seq_base = (long long)b * a.kv.seq_stride;
+  auto slot_of = [&](int pos) -> long long {
+    long long sl;
+    if constexpr (PAGED) {
+      const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
+      const int e = pt_lds[pg - pg0];  // the plan keeps every chunk within PT_CAP pages
+      sl = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
+    } else {
+      sl = seq_base + pos;
+    }
+    return (sl >= 0 && sl < a.kv.num_slots) ? sl : 0;  // unmapped positions read slot 0 (never visible)
+  };
+
+  // ---- copies of one block into ring slot `st` (K tile, then V tile)
+  const uint32_t ring_l =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem) +
+      (uint32_t)(wave * WRg::WAVE);
+  const long long slot_bytes = (long long)a.Hkv * WRg::ROWB;
+  const char* kg = reinterpret_cast<const char*>(a.kv.k) + (long long)g * WRg::ROWB;
+  const char* vg = reinterpret_cast<const char*>(a.kv.v) + (long long)g * WRg::ROWB;
+  uint32_t doff[WRg::LPT];  // per-lane offset of copy j inside a contiguous block
+  int drow[WRg::LPT], dcol[WRg::LPT];
+#pragma unroll
+  for (int j = 0; j < WRg::LPT; ++j) {
+    drow[j] = j * WRg::RPI + lane / WRg::CPR;
+    dcol[j] = ((lane % WRg::CPR) ^ swz<T, D>(drow[j])) * 16;
+    doff[j] = (uint32_t)(drow[j] * slot_bytes) + (uint32_t)dcol[j];
+  }
+  // copies of one tile (K if !is_v, else V) of block `blk` into ring slot `st`
+  auto issue = [&](int blk, int st, bool is_v) {
+    const int key0 = blk * 32;
+    const uint32_t ld = ring_l + (uint32_t)(st * WRg::BLK + (is_v ? WRg::TILE : 0));
+    const char* tg = is_v ? vg : kg;
+    if (!PAGED && key0 + 32 <= L && seq_base + key0 + 32 <= a.kv.num_slots) {
+      const char* bt = tg + (seq_base + key0) * slot_bytes;
+#pragma unroll
+      for (int j = 0; j < WRg::LPT; ++j) dma16_sbase(ld + j * 1024, doff[j], bt);
+    } else {
+#pragma unroll
+      for (int j = 0; j < WRg::LPT; ++j) {
+        const int pos = key0 + drow[j];
+        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < L ? pos : key0) * slot_bytes + dcol[j]);
+      }
+    }
+  };
+  const int nb = blk1 - blk0;
+  for (int i = 0; i < WRg::NSW && i < nb; ++i) {
+    issue(blk0 + i, i, false);
+    issue(blk0 + i, i, true);
+  }
+
+  // ---- query fragments (B operand of S^T = K Q^T): lane column = query row
+  bf16x8 qf[RT][QN];
+  int row_node[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 32 + lane32;
+    const bool ok = r < a.R;
+    const int t = ok ? r / a.G : a.N - 1;
+    row_node[rt] = t;
+    const int j = ok ? r % a.G : 0;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + ((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D;
+#pragma unroll
+    for (int ks = 0; ks < QN; ++ks) {
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * h);
+      qf[rt][ks] = ok ? x : bf16x8{};
+    }
+  }
+
+  // ---- score operand: scale * qbar_g split into bf16 hi + mid + lo = B columns 0..2
+  const bool wg_scores = a.do_scores && cblk0 * 32 < Pb;
+  bf16x8 qbf[QN];
+  if (wg_scores) {
+    if (a.prep_qbar) {
+      for (int d = tid; d < D; d += 256) qs[d] = a.ws_qbar[(b * a.Hkv + g) * D + d];
+    } else {
+      constexpr int NP = 256 / D;
+      const int d = tid % D, part = tid / D;
+      const int npairs = a.n_score_rows * a.G;
+      float acc = 0.f;
+#pragma unroll 4
+      for (int i = part; i < npairs; i += NP) {
+        const int t = a.score_rows[i / a.G], j = i % a.G;
+        acc += (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + d];
+      }
+      qs[D + part * D + d] = acc;
+      __syncthreads();
+      if (tid < D) {
+        float sacc = 0.f;
+        for (int p = 0; p < NP; ++p) sacc += qs[D + p * D + tid];
+        qs[tid] = sacc;
+      }
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += 256) {
+      const float x = qs[d] * a.scale;
+      const bf16 hi = (bf16)x;
+      const float r1 = x - (float)hi;
+      const bf16 mid = (bf16)r1;
+      const bf16 lo = (bf16)(r1 - (float)mid);
+      qbt[d] = hi;
+      qbt[D + d] = mid;
+      qbt[2 * D + d] = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < QN; ++ks)
+      qbf[ks] = lane32 < 3 ? *reinterpret_cast<const bf16x8*>(qbt + lane32 * D + 16 * ks + 8 * h) : bf16x8{};
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < QN; ++ks) qbf[ks] = bf16x8{};
+  }
+
+  // ---- ancestor bitsets of this lane's rows (trees, for blocks holding verify tokens)
+  uint32_t anc[RT][kAncWords] = {};
+  if (a.tree && blk1 * 32 > Pb) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int w = 0; w < kAncWords; ++w) {
+        anc[rt][w] = a.ws_anc[((long long)b * a.N + row_node[rt]) * kAncWords + w];
+        asm volatile("" ::"v"(anc[rt][w]));  // wait for the load here, not inside the loop
+      }
+  }
+
+  // ---- per-lane LDS offsets of the operand reads inside a block
+  int koff[QN];
+#pragma unroll
+  for (int kr = 0; kr < QN; ++kr) koff[kr] = tile_off<T, D>(lane32, 2 * kr + h);
+  const int e4 = (lane & 15) >> 2, cq = lane & 3, dh = (lane >> 4) & 1;
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+      voff[db][hl] = tile_off<T, D>(4 * h + e4 + 8 * hl, 4 * db + 2 * dh + (cq >> 1)) + (cq & 1) * 8;
+
+  f32x16 o[RT][DB];
+  float m[RT], l[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = kNegInf;
+    l[rt] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rt][db] = f32x16{};
+  }
+  float* sdst = a.ws_s + ((long long)b * a.Hkv + g) * a.P_max;
+  float pend[16];
+  int pend_key = -1;  // first key of the block whose scores are pending (wave-uniform)
+  auto flush_scores = [&]() {
+    if (pend_key >= 0 && lane32 == 0) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int k0 = pend_key + 8 * qd + 4 * h;
+        if (k0 + 4 <= Pb) {
+          *reinterpret_cast<f32x4*>(sdst + k0) = f32x4{pend[4 * qd], pend[4 * qd + 1], pend[4 * qd + 2], pend[4 * qd + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (k0 + e < Pb) sdst[k0 + e] = pend[4 * qd + e];
+        }
+      }
+    }
+  };
+  const char* wring = smem + wave * WRg::WAVE;
+
+  for (int i = 0; i < nb; ++i) {
+    // block i has landed once only the copies of later blocks (and the score
+    // stores issued before them, see flush_scores) can still be outstanding;
+    // loads complete in order, so vmcnt <= later copies means block i is in LDS
+    wait_blocks_after<STEP>(min(WRg::NSW - 1, nb - 1 - i));
+    flush_scores();
+    const int st = i % WRg::NSW;
+    const int blk = blk0 + i;
+    const int key0 = blk * 32;
+    const char* Kb = wring + st * WRg::BLK;
+    const char* Vb = Kb + WRg::TILE;
+    const bool do_score = wg_scores && key0 < Pb;
+
+    f32x16 s[RT];
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) s[rt] = f32x16{};
+    {
+      bf16x8 ka[QN];
+#pragma unroll
+      for (int ks = 0; ks < QN; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(Kb + koff[ks]);
+      if (do_score) {
+#pragma unroll
+        for (int ks = 0; ks < QN; ++ks) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) s[rt] = mfma_bf16(ka[ks], qf[rt][ks], s[rt]);
+          sc = mfma_bf16(ka[ks], qbf[ks], sc);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < QN; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) s[rt] = mfma_bf16(ka[ks], qf[rt][ks], s[rt]);
+      }
+    }
+    // the K tile of this slot is consumed: refill it with block i + NSW (the
+    // wait makes sure every LDS read of it has returned before the copy starts)
+    if (i + WRg::NSW < nb) {
+      wait_lgkm0();
+      issue(blk + WRg::NSW, st, false);
+    }
+
+    if (do_score) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) pend[v] = sc[v] + row_shl<1>(sc[v]) + row_shl<2>(sc[v]);
+      pend_key = key0;
+    } else {
+      pend_key = -1;
+    }
+
+    // mask (blocks reaching the verify tokens): key j is visible iff j < P_b or
+    // j - P_b is an ancestor-or-self of the row's node (chains: j - P_b <= t);
+    // positions at or past P_b + N are never ancestors, so they drop out too
+    if (key0 + 32 > Pb) {
+      if (a.tree) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int an = key0 + kappa(v, h) - Pb;
+            uint32_t word = 0;
+#pragma unroll
+            for (int w = 0; w < kAncWords; ++w) word = ((an >> 5) == w) ? anc[rt][w] : word;
+            const bool vis = an < 0 || ((word >> (an & 31)) & 1u);
+            s[rt][v] = vis ? s[rt][v] : kNegInf;
+          }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int an = key0 + kappa(v, h) - Pb;
+            s[rt][v] = an <= row_node[rt] ? s[rt][v] : kNegInf;
+          }
+      }
+    }
+
+    // online softmax, log2 domain, lazy rescale
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = s[rt][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[rt][v]);
+      mx = half_max(mx) * a.scale_log2;
+      const bool grew = mx > m[rt] + kRescaleSlack;
+      if (__any(grew)) {
+        const float mn = grew ? mx : m[rt];
+        const float alpha = grew ? fast_exp2(m[rt] - mn) : 1.f;
+        l[rt] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rt][db] *= alpha;
+        m[rt] = mn;
+      }
+      const float mneg = m[rt] == kNegInf ? 0.f : -m[rt];
+      float psum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(__builtin_fmaf(s[rt][v], a.scale_log2, mneg));
+        s[rt][v] = p;
+        psum += p;
+      }
+      l[rt] += psum;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      bf16x8 pb[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pb[rt][u] = (bf16)s[rt][8 * jj + u];
+      const char* Vj = Vb + jj * 16 * WRg::ROWB;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x4 lo = lds_read_tr16(reinterpret_cast<const T*>(Vj + voff[db][0]));
+        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const T*>(Vj + voff[db][1]));
+        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[rt][db] = mfma_bf16(va, pb[rt], o[rt][db]);
+      }
+    }
+    if (i + WRg::NSW < nb) {  // likewise for the V tile
+      wait_lgkm0();
+      issue(blk + WRg::NSW, st, true);
+    }
+  }
+  flush_scores();
+
+  // ---- epilogue: combine the four waves (same rows, disjoint keys), write (m, l, o) partials
+  wait_vm_lgkm0<0>();
+  __syncthreads();
+  constexpr int OS = D + 1;
+  float* lo_ = reinterpret_cast<float*>(smem);  // [4 waves][32 rows][D+1]
+  float* lml = lo_ + 4 * 32 * OS;                // [4 waves][32 rows][2]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float lt = half_sum(l[rt]);
+    if (rt > 0) __syncthreads();
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) lo_[(wave * 32 + lane32) * OS + 32 * db + kappa(v, h)] = o[rt][db][v];
+    if (h == 0) {
+      lml[(wave * 32 + lane32) * 2 + 0] = m[rt];
+      lml[(wave * 32 + lane32) * 2 + 1] = lt;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 32 * D; idx += 256) {
+      const int d = idx % D, r = idx / D;
+      const int row = rt * 32 + r;
+      if (row >= a.R) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, lml[(w * 32 + r) * 2]);
+      float acc = 0.f, lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = lml[(w * 32 + r) * 2];
+        const float wt = (M == kNegInf) ? 0.f : fast_exp2(mw - M);
+        acc += wt * lo_[(w * 32 + r) * OS + d];
+        lsum += wt * lml[(w * 32 + r) * 2 + 1];
+      }
+      const long long rec = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks + c;
+      a.ws_o[rec * D + d] = acc;
+      if (d == 0) a.ws_ml[rec] = f32x2{M, lsum};
+    }
+  }
+}
+
 __device__ __forceinline__ float block_reduce_max(float x, float* red) {
   x = wave_max(x);
   __syncthreads();
@@ -563,7 +1015,7 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
     const int row = gr % a.R, bg = gr / a.R, g = bg % a.Hkv, b = bg / a.Hkv;
     int Pb = a.prefix_len[b];
     Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
-    const int nc = min((Pb + a.N + a.chunk - 1) / a.chunk, a.n_chunks);
+    const int nc = a.all_chunks ? a.n_chunks : min((Pb + a.N + a.chunk - 1) / a.chunk, a.n_chunks);
     const long long rec0 = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks;
     float mloc = kNegInf;
     for (int c = tid; c < nc; c += 256) mloc = fmaxf(mloc, a.ws_ml[rec0 + c][0]);
@@ -675,21 +1127,53 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   VerifyPlan p{};
   p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.D = D; p.P_max = P_max; p.dtype = dtype;
   p.R = N * p.G;
-  const int rtiles = (p.R + 31) / 32;
-  if (rtiles <= 1) { p.RT = 1; p.WR = 1; }
-  else if (rtiles <= 2) { p.RT = 2; p.WR = 1; }
-  else if (rtiles <= 4) { p.RT = 2; p.WR = 2; }
-  else { p.RT = 2; p.WR = 4; }
-  p.WK = 4 / p.WR;
-  p.rows_per_block = p.RT * p.WR * 32;
-  p.RB = (p.R + p.rows_per_block - 1) / p.rows_per_block;
-  p.Rpad = p.RB * p.rows_per_block;
   const int es = dtype == SV_BF16 ? 2 : 4;
+  const long long Lmax = (long long)P_max + N;
+  p.tree = tree;
+  p.scores = n_score_rows > 0;
+  p.prep_qbar = p.scores && (long long)n_score_rows * p.G > kInlineQbarRows;
+  p.prep = p.prep_qbar || tree;
+  p.stream = dtype == SV_BF16 && p.R <= 64;
+  if (p.stream) {
+    // streaming kernel: waves split the keys of one (sequence, KV head) chunk
+    p.RT = p.R <= 32 ? 1 : 2;
+    p.WR = 1;
+    p.WK = 4;
+    p.rows_per_block = p.RT * 32;
+    p.RB = 1;
+    p.Rpad = p.rows_per_block;
+    p.TK = 32;
+    const long long units = (long long)B * Hkv;
+    const long long nbk = (Lmax + 31) / 32;
+    long long want = (256 + units / 2) / units;
+    if (want < 1) want = 1;
+    if (want > (nbk + 3) / 4) want = (nbk + 3) / 4;  // at least one block per wave on average
+    if (page_size > 0) {  // a chunk's page-table slice must fit the LDS copy (PT_CAP entries)
+      const long long cap_blocks = ((long long)(WaveRing<128>::PT_CAP - 2) * page_size) / 32 - 1;
+      const long long need = (nbk + cap_blocks - 1) / (cap_blocks > 0 ? cap_blocks : 1);
+      if (want < need) want = need;
+    }
+    if (want > kMaxChunks) want = kMaxChunks;
+    if (want < 1) want = 1;
+    p.n_chunks = (int)want;
+    p.chunk = (int)(((nbk + want - 1) / want + 1) * 32);  // longest chunk, in keys
+    p.n_wg = (int)((units * p.n_chunks + 7) / 8 * 8);
+  }
+  const int rtiles = (p.R + 31) / 32;
+  if (!p.stream) {
+    if (rtiles <= 1) { p.RT = 1; p.WR = 1; }
+    else if (rtiles <= 2) { p.RT = 2; p.WR = 1; }
+    else if (rtiles <= 4) { p.RT = 2; p.WR = 2; }
+    else { p.RT = 2; p.WR = 4; }
+    p.WK = 4 / p.WR;
+    p.rows_per_block = p.RT * p.WR * 32;
+    p.RB = (p.R + p.rows_per_block - 1) / p.rows_per_block;
+    p.Rpad = p.RB * p.rows_per_block;
+  }
   const int SK = D * es > 256 ? 32 : 64;  // keys per ring stage (Ring<T, D>::SK)
   p.TK = SK;
   // one resident workgroup per CU (two for the smaller bf16, D = 64 ring)
   const int occ = (dtype == SV_BF16 && D == 64) ? 2 : 1;
-  const long long Lmax = (long long)P_max + N;
   const long long units = (long long)B * Hkv * p.RB;
   const long long target = 256LL * occ;
   long long want = (target + units / 2) / units;
@@ -702,14 +1186,12 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
     const long long cap = (long long)(Ring<float, 64>::PT_CAP - 2) * page_size / SK * SK;
     if (chunk > cap) chunk = cap < SK ? SK : cap;
   }
-  p.chunk = (int)chunk;
-  p.n_chunks = (int)((Lmax + chunk - 1) / chunk);
-  long long n_units = units * p.n_chunks;
-  p.n_wg = (int)((n_units + 7) / 8 * 8);
-  p.tree = tree;
-  p.scores = n_score_rows > 0;
-  p.prep_qbar = p.scores && (long long)n_score_rows * p.G > kInlineQbarRows;
-  p.prep = p.prep_qbar || tree;
+  if (!p.stream) {
+    p.chunk = (int)chunk;
+    p.n_chunks = (int)((Lmax + chunk - 1) / chunk);
+    long long n_units = units * p.n_chunks;
+    p.n_wg = (int)((n_units + 7) / 8 * 8);
+  }
   size_t off = 0;
   p.off_o = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * D * 4);
   p.off_ml = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * 8);
@@ -734,6 +1216,20 @@ static void launch_main(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st
   else launch_main2<T, D, RT, WR, false>(p, a, st, ev0, ev1);
 }
 
+template <int D, int RT, bool PAGED>
+static void launch_stream2(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL((verify_stream<D, RT, PAGED>), dim3(p.n_wg), dim3(256), 0, st, (hipEvent_t)ev0,
+                          (hipEvent_t)ev1, 0, a);
+  else
+    hipLaunchKernelGGL((verify_stream<D, RT, PAGED>), dim3(p.n_wg), dim3(256), 0, st, a);
+}
+template <int D, int RT>
+static void launch_stream(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
+  if (a.kv.page_table) launch_stream2<D, RT, true>(p, a, st, ev0, ev1);
+  else launch_stream2<D, RT, false>(p, a, st, ev0, ev1);
+}
+
 template <typename T, int D>
 static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
   if (p.prep) {
@@ -741,7 +1237,14 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
     const int nt = p.tree ? p.B : 0;
     hipLaunchKernelGGL((verify_prep<T, D>), dim3(nq + nt), dim3(256), 0, st, a, nq);
   }
-  if (p.RT == 1 && p.WR == 1) launch_main<T, D, 1, 1>(p, a, st, ev0, ev1);
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (p.stream) {
+      if (p.RT == 1) launch_stream<D, 1>(p, a, st, ev0, ev1);
+      else launch_stream<D, 2>(p, a, st, ev0, ev1);
+    }
+  }
+  if (p.stream) {
+  } else if (p.RT == 1 && p.WR == 1) launch_main<T, D, 1, 1>(p, a, st, ev0, ev1);
   else if (p.RT == 2 && p.WR == 1) launch_main<T, D, 2, 1>(p, a, st, ev0, ev1);
   else if (p.RT == 2 && p.WR == 2) launch_main<T, D, 2, 2>(p, a, st, ev0, ev1);
   else launch_main<T, D, 2, 4>(p, a, st, ev0, ev1);
@@ -770,6 +1273,7 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
   a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.R = p.R; a.RB = p.RB; a.Rpad = p.Rpad;
   a.P_max = p.P_max; a.chunk = p.chunk; a.n_chunks = p.n_chunks;
   a.n_units = p.B * p.Hkv * p.RB * p.n_chunks;
+  a.all_chunks = p.stream ? 1 : 0;
   a.ps_shift = -1;
   if (kv.page_table && kv.page_size > 0 && (kv.page_size & (kv.page_size - 1)) == 0) {
     a.ps_shift = 0;
