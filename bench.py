@@ -108,6 +108,8 @@ def main():
     sws_n = sv.sparse_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, kmax)
     vws = torch.empty(max(1, vws_n), dtype=torch.uint8, device=dev)
     sws = torch.empty(max(1, sws_n), dtype=torch.uint8, device=dev)
+    tws_n = sv.topk_workspace_size(wl.B, wl.P_max)
+    tws = torch.empty(max(1, tws_n), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
@@ -119,7 +121,7 @@ def main():
               parent.data_ptr() if parent is not None else None, rows_arr, len(rows), 0.0, out.data_ptr(),
               scores.data_ptr(), vws.data_ptr(), vws_n, sp) for kv in kvs]
     targs = (scores.data_ptr(), wl.B, wl.P_max, P.data_ptr(), ksel.data_ptr(), kmax, idx.data_ptr(),
-             count.data_ptr(), None, 0, sp)
+             count.data_ptr(), tws.data_ptr(), tws_n, sp)
     dargs = [[(dqs[s].data_ptr(), dt, wl.B, wl.Hq, wl.Hkv, wl.D, ctypes.byref(kv), idx.data_ptr(), kmax,
                count.data_ptr(), kmax, 0.0, douts[s].data_ptr(), sws.data_ptr(), sws_n, sp)
               for s in range(n_draft)] for kv in kvs]

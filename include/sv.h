@@ -141,7 +141,8 @@ sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, in
  *                order, then -1 up to k_max.  Ties are broken toward the lower
  *                index; -0.0 and +0.0 are equal.  Scores must be finite.
  *   count        device int32[B] (may be NULL): k'_b.
- *   workspace    sv_topk_workspace_size(B, P_max) bytes (may be 0 / NULL if that is 0).
+ *   workspace    sv_topk_workspace_size(B, P_max) bytes of device scratch (currently
+ *                0: NULL is accepted); contents on entry are ignored.
  */
 size_t sv_topk_workspace_size(int B, int P_max);
 sv_status sv_topk_select(const float* scores, int B, int P_max, const int32_t* prefix_len,

@@ -100,7 +100,7 @@ def test_workspace_sizes_are_consistent():
     p16 = lib.sv_verify_workspace_size(2, 8, 32, 8, 128, 65536, _lib.SV_BF16, 0, 2, 16)
     assert p1 > p16 > 0
     assert lib.sv_sparse_workspace_size(1, 32, 8, 128, 2048) >= 32 * 32 * 128 * 4
-    assert lib.sv_topk_workspace_size(4, 131072) == 0
+    assert lib.sv_topk_workspace_size(4, 131072) == 0          # selection keeps its state on chip
 
 
 def test_topk_and_sparse_reject_bad_arguments():

@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import SvError, SV_F32, SV_BF16  # noqa: F401
 
 __all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn",
-           "verify_workspace_size", "sparse_workspace_size", "timing_events", "SvError", "lib"]
+           "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size", "timing_events", "SvError",
+           "lib"]
 
 
 def lib() -> ctypes.CDLL:
@@ -144,8 +145,13 @@ def verify_attn(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max
     return out, (scores if rows else None)
 
 
+def topk_workspace_size(B, P_max) -> int:
+    return int(lib().sv_topk_workspace_size(B, P_max))
+
+
 def topk_select(scores: torch.Tensor, prefix_len: torch.Tensor, k: torch.Tensor, k_max: int,
-                idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None):
+                idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                workspace: Optional[Workspace] = None):
     """sv_topk_select: -> (idx int32 [B][k_max] ascending, -1 padded; count int32 [B])."""
     L = lib()
     B, P_max = (int(x) for x in scores.shape)
@@ -153,8 +159,9 @@ def topk_select(scores: torch.Tensor, prefix_len: torch.Tensor, k: torch.Tensor,
         idx = torch.empty((B, k_max), dtype=torch.int32, device=scores.device)
     if count is None:
         count = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    wptr, wlen = _ws(workspace, "topk").get(topk_workspace_size(B, P_max), scores.device)
     _lib.check(L.sv_topk_select(_ptr(scores), B, P_max, _ptr(prefix_len), _ptr(k), k_max, _ptr(idx), _ptr(count),
-                                None, 0, _stream(scores.device)))
+                                wptr, wlen, _stream(scores.device)))
     return idx, count
 
 

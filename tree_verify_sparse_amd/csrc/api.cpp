@@ -131,21 +131,21 @@ sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, in
 }
 
 size_t sv_topk_workspace_size(int B, int P_max) {
-  (void)B;
-  (void)P_max;
-  return 0;
+  if (B <= 0 || P_max < 0 || !sv::topk_supported(P_max)) return 0;
+  return sv::topk_workspace_bytes(B, P_max);
 }
 
 sv_status sv_topk_select(const float* scores, int B, int P_max, const int32_t* prefix_len, const int32_t* k,
                          int k_max, int32_t* idx, int32_t* count, void* workspace, size_t workspace_bytes,
                          sv_stream stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (B < 0 || P_max < 0 || k_max < 0) return fail(SV_E_INVALID, "B, P_max and k_max must be >= 0");
   if (B == 0) return ok();
   if (!scores || !prefix_len || !k || (!idx && k_max > 0))
     return fail(SV_E_INVALID, "scores, prefix_len, k and idx must be non-NULL");
-  return hip_status(sv::launch_topk(scores, B, P_max, prefix_len, k, k_max, idx, count, stream),
+  const size_t need = sv::topk_workspace_bytes(B, P_max);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+  return hip_status(sv::launch_topk(scores, B, P_max, prefix_len, k, k_max, idx, count, workspace, stream),
                     "sv_topk_select launch");
 }
 

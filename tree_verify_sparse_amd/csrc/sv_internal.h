@@ -53,7 +53,9 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
                   void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop);
 int launch_topk(const float* scores, int B, int P_max, const int32_t* prefix_len, const int32_t* k,
-                int k_max, int32_t* idx, int32_t* count, void* stream);
+                int k_max, int32_t* idx, int32_t* count, void* ws, void* stream);
+size_t topk_workspace_bytes(int B, int P_max);
+bool topk_supported(int P_max);
 int launch_sparse(const SparsePlan& p, int dtype, const void* q, const KvArgs& kv, const int32_t* idx,
                   int idx_stride, const int32_t* n_idx, float scale, void* out, void* ws, void* stream);
 
