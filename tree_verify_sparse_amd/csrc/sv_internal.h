@@ -11,6 +11,7 @@ namespace sv {
 constexpr int kMaxNodes = 256;       // verify nodes per sequence
 constexpr int kAncWords = 8;         // ancestor bitset words per node (256 bits)
 constexpr int kInlineQbarRows = 64;  // scoring (row, head) pairs summed inside the main kernel
+constexpr int kQbarPairs = 64;       // pairs per partial sum when a prep kernel forms qbar
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -22,6 +23,7 @@ struct VerifyPlan {
   int RT, WR, WK;   // row tiles per wave, waves along rows, waves along keys (WR*WK = 4)
   int rows_per_block, RB, Rpad;
   int TK;           // keys per LDS tile
+  int qsplit;       // qbar partial sums per (sequence, KV head) (prep_qbar only)
   int chunk;        // keys per split of the KV range
   int n_chunks;     // splits covering the longest sequence (P_max + N)
   int n_wg;         // workgroups of the main kernel (multiple of 8)

@@ -88,6 +88,7 @@ struct VerifyArgs {
   float* scores;
   int B, N, Hq, Hkv, G, R, RB, Rpad, P_max, chunk, n_chunks, n_units;
   int tree, do_scores, prep_qbar;
+  int qsplit;  // prep_qbar: partial sums per (sequence, KV head), each over kQbarPairs (row, head) pairs
   int all_chunks;  // every chunk writes a partial (streaming kernel), else only chunks below P_b + N
   int ps_shift;  // log2(page_size) if it is a power of two, else -1
   float scale, scale_log2;
@@ -232,7 +233,12 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   const bool wg_scores = a.do_scores && rb == 0 && c0 < Pb;
   if (wg_scores) {
     if (a.prep_qbar) {
-      for (int d = tid; d < D; d += 256) qs[d] = a.ws_qbar[(b * a.Hkv + g) * D + d];
+      for (int d = tid; d < D; d += 256) {
+        const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
+        float acc = 0.f;
+        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];
+        qs[d] = acc;
+      }
     } else {
       constexpr int NP = 256 / D;
       const int d = tid % D, part = tid / D;
@@ -722,7 +728,12 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
   bf16x8 qbf[QN];
   if (wg_scores) {
     if (a.prep_qbar) {
-      for (int d = tid; d < D; d += 256) qs[d] = a.ws_qbar[(b * a.Hkv + g) * D + d];
+      for (int d = tid; d < D; d += 256) {
+        const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
+        float acc = 0.f;
+        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];
+        qs[d] = acc;
+      }
     } else {
       constexpr int NP = 256 / D;
       const int d = tid % D, part = tid / D;
@@ -1068,21 +1079,26 @@ __global__ void __launch_bounds__(256) verify_prep(const VerifyArgs a, int n_qba
   __shared__ uint32_t ancs[2][kMaxNodes][kAncWords];
   __shared__ int jmp[2][kMaxNodes];
   if ((int)blockIdx.x < n_qbar_wgs) {
-    const int g = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+    // partial qbar of (b, g) over pairs [sp * kQbarPairs, (sp + 1) * kQbarPairs):
+    // D columns x (256 / D) pair phases, loads unrolled so they are in flight together
+    const int sp = blockIdx.x % a.qsplit, bg = blockIdx.x / a.qsplit;
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
     constexpr int NP = 256 / D;
     const int d = tid % D, p = tid / D;
     const int npairs = a.n_score_rows * a.G;
+    const int i_end = min(npairs, (sp + 1) * kQbarPairs);
     float acc = 0.f;
-    for (int i = p; i < npairs; i += NP) {
+#pragma unroll 8
+    for (int i = sp * kQbarPairs + p; i < i_end; i += NP) {
       const int t = a.score_rows[i / a.G], j = i % a.G;
       acc += (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + d];
     }
     part[tid] = acc;
     __syncthreads();
     if (tid < D) {
-      float s = 0.f;
-      for (int k = 0; k < NP; ++k) s += part[k * D + tid];
-      a.ws_qbar[(b * a.Hkv + g) * D + tid] = s;
+      float sum = 0.f;
+      for (int k = 0; k < NP; ++k) sum += part[k * D + tid];
+      a.ws_qbar[((long long)bg * a.qsplit + sp) * D + tid] = sum;
     }
     return;
   }
@@ -1132,6 +1148,7 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   p.tree = tree;
   p.scores = n_score_rows > 0;
   p.prep_qbar = p.scores && (long long)n_score_rows * p.G > kInlineQbarRows;
+  p.qsplit = p.prep_qbar ? (n_score_rows * p.G + kQbarPairs - 1) / kQbarPairs : 0;
   p.prep = p.prep_qbar || tree;
   p.stream = dtype == SV_BF16 && p.R <= 64;
   if (p.stream) {
@@ -1196,7 +1213,7 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   p.off_o = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * D * 4);
   p.off_ml = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * 8);
   p.off_s = off; off = align_up(off + (p.scores ? (size_t)B * Hkv * P_max * 4 : 0));
-  p.off_qbar = off; off = align_up(off + (p.prep_qbar ? (size_t)B * Hkv * D * 4 : 0));
+  p.off_qbar = off; off = align_up(off + (p.prep_qbar ? (size_t)B * Hkv * p.qsplit * D * 4 : 0));
   p.off_anc = off; off = align_up(off + (tree ? (size_t)B * N * kAncWords * 4 : 0));
   p.bytes = off;
   return p;
@@ -1233,7 +1250,7 @@ static void launch_stream(const VerifyPlan& p, const VerifyArgs& a, hipStream_t 
 template <typename T, int D>
 static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
   if (p.prep) {
-    const int nq = p.prep_qbar ? p.B * p.Hkv : 0;
+    const int nq = p.prep_qbar ? p.B * p.Hkv * p.qsplit : 0;
     const int nt = p.tree ? p.B : 0;
     hipLaunchKernelGGL((verify_prep<T, D>), dim3(nq + nt), dim3(256), 0, st, a, nq);
   }
@@ -1279,7 +1296,7 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
     a.ps_shift = 0;
     while ((1 << a.ps_shift) < kv.page_size) ++a.ps_shift;
   }
-  a.tree = p.tree; a.do_scores = p.scores; a.prep_qbar = p.prep_qbar;
+  a.tree = p.tree; a.do_scores = p.scores; a.prep_qbar = p.prep_qbar; a.qsplit = p.qsplit;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.n_score_rows = n_score_rows;
