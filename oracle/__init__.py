@@ -24,6 +24,7 @@ from .reference import (  # noqa: F401
     visible_positions,
     verify_attention,
     verify_scores,
+    verify_scores_grouped,
     topk_select,
     sparse_draft_attention,
     run_step,

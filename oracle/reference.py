@@ -27,6 +27,7 @@ Pins (tests/test_oracle_*.py):
                           star tree == prefix + root + self; N = 1 == decode
   verify_scores        -- closed form scale * sum_g K_g . qbar_g; golden values;
                           linearity; all-rows == union of per-row scores
+  verify_scores_grouped -- equal to verify_scores (relative 1e-12) on the pin cases
   topk_select          -- brute-force enumeration of all k-subsets (Vegas §2.A
                           argmax) on tiny inputs with exact ties; golden cases
   sparse_draft_attention -- idx = whole prefix == dense decode; permutation
@@ -188,6 +189,31 @@ def verify_scores(q: np.ndarray, dtype: str, kv: KVCache, P: np.ndarray,
             for t in rows:
                 for h in range(g * G, (g + 1) * G):
                     acc += scale * (Kg @ qf[b, t, h])              # logits of entry i for (t, h)
+        s[b, :Pb] = acc
+    return s
+
+
+def verify_scores_grouped(q: np.ndarray, dtype: str, kv: KVCache, P: np.ndarray,
+                          score_rows: Sequence[int], scale: float, Hkv: int,
+                          P_max: Optional[int] = None) -> np.ndarray:
+    """The same sum as verify_scores, grouped: every logit is linear in q, so
+    the sum over rows t and the heads h of KV group g can be taken over the
+    queries first, s_{b,i} = scale * sum_g k_{b,i,g} . (sum_{t, h in g} q_{b,t,h}).
+    One product per (sequence, KV head) instead of one per (row, head), which
+    makes full-size checks affordable; pinned to verify_scores on small inputs."""
+    qf = _f64(q, dtype)
+    B, N, Hq, D = qf.shape
+    G = Hq // Hkv
+    if P_max is None:
+        P_max = int(np.max(P)) if B else 0
+    s = np.full((B, P_max), np.nan)
+    rows = [int(t) for t in score_rows]
+    for b in range(B):
+        Pb = int(P[b])
+        acc = np.zeros(Pb)
+        for g in range(Hkv):
+            qsum = qf[b, rows][:, g * G:(g + 1) * G].sum(axis=(0, 1))   # [D]
+            acc += scale * (kv.keys(b, g, np.arange(Pb)) @ qsum)
         s[b, :Pb] = acc
     return s
 

@@ -180,6 +180,9 @@ def test_scores_closed_form(case):
         ref = wl.scale * np.einsum("igd,gd->i", Kb, qbar)
         np.testing.assert_allclose(s[b, :Pb], ref, rtol=1e-10, atol=1e-12)
         assert np.isnan(s[b, Pb:]).all()
+    # the grouped oracle routine (used for full-size checks) is the same sum
+    sg = oracle.verify_scores_grouped(wl.q, wl.dtype, KVCache.of(wl), wl.P, wl.score_rows, wl.scale, wl.Hkv)
+    np.testing.assert_allclose(sg, s, rtol=1e-10, atol=1e-12)
 
 
 def test_scores_linear_in_rows_and_c2q_subset():

@@ -11,7 +11,9 @@ Storage conventions (shared by the oracle and the HIP path):
 * The N verify tokens of sequence b (the root/last committed token followed by
   the drafted nodes) have their own K/V at logical positions ``[P_b, P_b + N)``.
 
-Value recipe: Q, K and V entries are N(0, sigma^2) with sigma = 1/sqrt(D).
+Value recipe: Q, K and V entries are N(0, sigma^2) with sigma = 1/sqrt(D);
+K and V of sequence b are drawn in blocks of 16384 tokens, block j from its
+own stream (seed, tensor, b, j), so generation can fill blocks in parallel.
 Planted heavy keys (workloads 1, 2 and 4): a key chosen as heavy gets
 ``+c * sigma * u_{b,g}`` added in every KV head g, where ``u_{b,g}`` is the unit
 vector along the sum of the sequence's scoring-row queries of the heads that
@@ -23,6 +25,7 @@ drawn without replacement from ``[0, P - 64)``; workloads 2 and 4 also give the
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -98,6 +101,51 @@ class Workload:
 
 def _draw(rng: np.random.Generator, shape, std: float) -> np.ndarray:
     return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+_CHUNK = 16384  # tokens per independently seeded block of a K or V draw
+
+
+def _pool():
+    import concurrent.futures
+    global _POOL
+    if _POOL is None:
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+_POOL = None
+
+
+def _draw_blocks(seed_words, shape, std: float) -> np.ndarray:
+    """N(0, std^2) float32 array of `shape`, drawn in blocks of _CHUNK rows along
+    axis 0, block j from its own stream SeedSequence(seed_words + [j]); the
+    values depend only on the seed, not on how many threads fill them."""
+    out = np.empty(shape, dtype=np.float32)
+    n = shape[0]
+
+    def fill(j):
+        r = np.random.default_rng(np.random.SeedSequence([int(x) for x in seed_words] + [j]))
+        blk = out[j * _CHUNK: min(n, (j + 1) * _CHUNK)]
+        r.standard_normal(size=blk.shape, dtype=np.float32, out=blk)
+        blk *= np.float32(std)
+
+    list(_pool().map(fill, range((n + _CHUNK - 1) // _CHUNK)))
+    return out
+
+
+def _store_blocks(x: np.ndarray, dtype: str) -> np.ndarray:
+    """_store applied block-wise in the thread pool (same result)."""
+    if dtype == "f32" or x.shape[0] <= _CHUNK:
+        return _store(x, dtype)
+    out = np.empty(x.shape, dtype=np.uint16)
+
+    def conv(j):
+        sl = slice(j * _CHUNK, min(x.shape[0], (j + 1) * _CHUNK))
+        out[sl] = bf16_bits_from_f32(x[sl])
+
+    list(_pool().map(conv, range((x.shape[0] + _CHUNK - 1) // _CHUNK)))
+    return out
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -201,12 +249,12 @@ def make_custom(*, seed, B=1, Hq=4, Hkv=1, D=64, dtype="f32", P=512, N=5,
 
     G = Hq // Hkv
     kstore = np.zeros((num_slots, Hkv, D), dtype=np.float32 if dtype == "f32" else np.uint16)
-    vstore = np.zeros_like(kstore)
-    rk, rv = rng(_S_K), rng(_S_V)
+    vstore = np.zeros((num_slots, Hkv, D), dtype=kstore.dtype)
+    seed_words = [int(x) for x in np.atleast_1d(seed)]
     for b in range(B):
         Lb = int(L[b])
-        kb = _draw(rk, (Lb, Hkv, D), sigma)
-        vb = _draw(rv, (Lb, Hkv, D), sigma)
+        kb = _draw_blocks(seed_words + [_S_K, b], (Lb, Hkv, D), sigma)
+        vb = _draw_blocks(seed_words + [_S_V, b], (Lb, Hkv, D), sigma)
         if heavy is not None or window > 0:
             # direction along the sum of the scoring rows' queries, per KV head
             qsum = qv[b][rows].reshape(len(rows), Hkv, G, D).sum(axis=(0, 2)).astype(np.float64)
@@ -224,8 +272,8 @@ def make_custom(*, seed, B=1, Hq=4, Hkv=1, D=64, dtype="f32", P=512, N=5,
                 vb[int(Pb[b]) + t, :, t % D] = np.float32(v_canary * (1.0 + t / N))
         slots = (b * seq_stride + np.arange(Lb)) if layout == "contiguous" else (
             page_table[b].astype(np.int64)[np.arange(Lb) // page_size] * page_size + np.arange(Lb) % page_size)
-        kstore[slots] = _store(kb, dtype)
-        vstore[slots] = _store(vb, dtype)
+        kstore[slots] = _store_blocks(kb, dtype)
+        vstore[slots] = _store_blocks(vb, dtype)
 
     dq = _store(_draw(rng(_S_DQ), (decode_steps, B, Hq, D), sigma * q_std_mult), dtype)
 
