@@ -198,7 +198,10 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     # bf16 with at most 64 query rows per KV head runs the key-split streaming kernel
-    roof["kernel"] = "verify_stream" if (wl.dtype == "bf16" and wl.N * (wl.Hq // wl.Hkv) <= 64) else "verify_main"
+    if wl.dtype == "bf16":  # bf16: key-split streaming kernel up to 64 rows per KV head, tree kernel above
+        roof["kernel"] = "verify_stream" if wl.N * (wl.Hq // wl.Hkv) <= 64 else "verify_tree"
+    else:
+        roof["kernel"] = "verify_main"
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
     roof["algorithmic_bytes"] = verify_bytes
     roof["algorithmic_flops"] = verify_flops

@@ -29,6 +29,7 @@ struct VerifyPlan {
   int n_wg;         // workgroups of the main kernel (multiple of 8)
   bool tree, scores, prep_qbar, prep;
   bool stream;      // bf16 with R <= 64: the key-split streaming kernel (verify_stream)
+  bool treek;       // bf16 with R > 64: the eight-wave row-split tree kernel (verify_tree)
   size_t off_o, off_ml, off_s, off_qbar, off_anc, bytes;
 };
 

@@ -89,6 +89,7 @@ struct VerifyArgs {
   int B, N, Hq, Hkv, G, R, RB, Rpad, P_max, chunk, n_chunks, n_units;
   int tree, do_scores, prep_qbar;
   int qsplit;  // prep_qbar: partial sums per (sequence, KV head), each over kQbarPairs (row, head) pairs
+  int s_stride;  // row stride of the per-KV-head score partials: P_max + 32 (whole blocks are stored)
   int all_chunks;  // every chunk writes a partial (streaming kernel), else only chunks below P_b + N
   int ps_shift;  // log2(page_size) if it is a power of two, else -1
   float scale, scale_log2;
@@ -134,9 +135,11 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   int Pb = a.prefix_len[b];
   Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
   const int L = Pb + a.N;
-  const int c0 = c * a.chunk;
-  if (c0 >= L) return;
-  const int c1 = min(c0 + a.chunk, L);
+  // chunk c covers stages [c * nst / n_chunks, (c + 1) * nst / n_chunks) of
+  // this sequence (balanced; an empty chunk still writes an empty partial)
+  const int nst_seq = (L + RG::SK - 1) / RG::SK;
+  const int c0 = (int)((long long)c * nst_seq / a.n_chunks) * RG::SK;
+  const int c1 = min((int)((long long)(c + 1) * nst_seq / a.n_chunks) * RG::SK, L);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lane32 = lane & 31, h = lane >> 5;
@@ -181,7 +184,7 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
     const int cl = (lane % RG::CPR) ^ swz<T, D>(dma_row[j]);
     dma_off[j] = (int)(dma_row[j] * slot_bytes) + cl * 16;
   }
-  const int n_st = (c1 - c0 + RG::SK - 1) / RG::SK;
+  const int n_st = c1 > c0 ? (c1 - c0 + RG::SK - 1) / RG::SK : 0;
   auto issue = [&](int i) {
     const int key0 = c0 + i * RG::SK;
     char* dst = ring + (i % RG::NS) * RG::STAGE + wave * RG::LPW * 1024;
@@ -230,7 +233,7 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
 
   // ---- score operand: qbar_g (fp32) split into bf16 hi + mid + lo, kept in
   // LDS as three rows; they become MFMA columns 0..2 of S^T's companion tile
-  const bool wg_scores = a.do_scores && rb == 0 && c0 < Pb;
+  const bool wg_scores = a.do_scores && c0 < Pb;  // key blocks are shared out over the row blocks
   if (wg_scores) {
     if (a.prep_qbar) {
       for (int d = tid; d < D; d += 256) {
@@ -333,18 +336,16 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
 
     const char* Kt = ring + (i % RG::NS) * RG::STAGE;
     const char* Vt = Kt + RG::TILE;
-#pragma unroll
-    for (int kb = 0; kb < RG::NB; ++kb) {
+    // S^T of block kb of this stage (and, for one wave of one row block per
+    // key block, the score columns)
+    auto qk_block = [&](int kb, f32x16 (&s)[RT]) {
       const int gb = i * RG::NB + kb;
-      if ((gb % WK) != wk) continue;
       const int kb0 = c0 + 32 * gb;
-      if (kb0 >= c1) break;
-      const bool do_score = wg_scores && kb0 < Pb && ((gb / WK) % WR) == wr;
+      const int jblk = kb0 >> 5;  // key block index within the sequence
+      const bool do_score = wg_scores && kb0 < Pb && (jblk % a.RB) == rb && ((jblk / a.RB) % WR) == wr;
       const char* Kb = Kt + kb * 32 * RG::ROWB;
-      const char* Vb = Vt + kb * 32 * RG::ROWB;
-
       // S^T = K Q^T in two independent accumulation chains (and the score columns)
-      f32x16 s[RT], s2[RT];
+      f32x16 s2[RT];
       f32x16 sc = f32x16{};
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -391,23 +392,21 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
           if constexpr (kBf16) x = x + row_shl<1>(sc[v]) + row_shl<2>(sc[v]);
           tv[v] = x * a.scale;
         }
-        if (lane32 == 0) {
-          const int lim = min(Pb, c1);
-          float* dst = a.ws_s + ((long long)b * a.Hkv + g) * a.P_max;
+        if (lane32 == 0) {  // whole block (rows are padded by 32; entries past P_b are never read)
+          float* dst = a.ws_s + ((long long)b * a.Hkv + g) * a.s_stride;
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int k0 = kb0 + 8 * qd + 4 * h;
-            if (k0 + 4 <= lim) {
-              *reinterpret_cast<f32x4*>(dst + k0) = f32x4{tv[4 * qd], tv[4 * qd + 1], tv[4 * qd + 2], tv[4 * qd + 3]};
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (k0 + e < lim) dst[k0 + e] = tv[4 * qd + e];
-            }
-          }
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<f32x4*>(dst + kb0 + 8 * qd + 4 * h) =
+                f32x4{tv[4 * qd], tv[4 * qd + 1], tv[4 * qd + 2], tv[4 * qd + 3]};
         }
       }
 
+    };
+    // mask, online softmax and O^T += V^T P^T of block kb
+    auto finish_block = [&](int kb, f32x16 (&s)[RT]) {
+      const int gb = i * RG::NB + kb;
+      const int kb0 = c0 + 32 * gb;
+      const char* Vb = Vt + kb * 32 * RG::ROWB;
       // mask: keys past the chunk end, and verify tokens that are not ancestors-or-self
       if (kb0 + 32 > min(Pb, c1)) {
         if (a.tree) {
@@ -494,6 +493,28 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
             for (int rt = 0; rt < RT; ++rt) o[rt][db] = mfma_f32(va, s[rt][v], o[rt][db]);
           }
         }
+      }
+    };
+    if constexpr (WK == 1) {
+      // every wave takes every block of the stage: issue both blocks' S^T
+      // products before the first softmax so the matrix cores stay busy
+      // while the vector unit works
+      f32x16 sb[RG::NB][RT];
+#pragma unroll
+      for (int kb = 0; kb < RG::NB; ++kb)
+        if (c0 + 32 * (i * RG::NB + kb) < c1) qk_block(kb, sb[kb]);
+#pragma unroll
+      for (int kb = 0; kb < RG::NB; ++kb)
+        if (c0 + 32 * (i * RG::NB + kb) < c1) finish_block(kb, sb[kb]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < RG::NB; ++kb) {
+        const int gb = i * RG::NB + kb;
+        if ((gb % WK) != wk) continue;
+        if (c0 + 32 * gb >= c1) break;
+        f32x16 s[RT];
+        qk_block(kb, s);
+        finish_block(kb, s);
       }
     }
   }
@@ -805,22 +826,15 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[rt][db] = f32x16{};
   }
-  float* sdst = a.ws_s + ((long long)b * a.Hkv + g) * a.P_max;
+  float* sdst = a.ws_s + ((long long)b * a.Hkv + g) * a.s_stride;
   float pend[16];
   int pend_key = -1;  // first key of the block whose scores are pending (wave-uniform)
-  auto flush_scores = [&]() {
+  auto flush_scores = [&]() {  // whole block (rows are padded by 32; entries past P_b are never read)
     if (pend_key >= 0 && lane32 == 0) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int k0 = pend_key + 8 * qd + 4 * h;
-        if (k0 + 4 <= Pb) {
-          *reinterpret_cast<f32x4*>(sdst + k0) = f32x4{pend[4 * qd], pend[4 * qd + 1], pend[4 * qd + 2], pend[4 * qd + 3]};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (k0 + e < Pb) sdst[k0 + e] = pend[4 * qd + e];
-        }
-      }
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<f32x4*>(sdst + pend_key + 8 * qd + 4 * h) =
+            f32x4{pend[4 * qd], pend[4 * qd + 1], pend[4 * qd + 2], pend[4 * qd + 3]};
     }
   };
   const char* wring = smem + wave * WRg::WAVE;
@@ -995,6 +1009,321 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tree kernel for many query rows per KV head (bf16, N * G > 64: draft trees
+// and long chains).  Eight waves per workgroup, each owning one 32-row tile of
+// a block of 256 rows; all waves read the same K/V tiles from a 4-stage LDS
+// ring that they fill together (global->LDS copies, one barrier per stage).
+// Two waves share each SIMD, so one wave's softmax runs on the vector unit
+// while the other's products run on the matrix cores, and within a wave both
+// blocks' S^T products of a stage are issued before the first softmax.  No two
+// waves hold the same rows, so each writes its own (m, l, o) partials.
+constexpr int kTreeWaves = 8;
+
+template <int D, bool PAGED>
+__global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs a) {
+  using T = bf16;
+  using RG = Ring<T, D>;
+  constexpr int NW = kTreeWaves, NT = 64 * NW;
+  constexpr int DB = D / 32, QN = D / 16;
+  constexpr int LPW = RG::SEGS / NW;  // 1 KB copies per wave per stage
+  static_assert(LPW * NW == RG::SEGS && LPW >= 1, "ring split over the waves");
+  constexpr int QB4 = 4 * D * 2;      // score operand rows: qbar hi, mid, lo and a zero row
+  constexpr int LDS = RG::MAIN + RG::PT_CAP * 4 + RG::AUX_FLOATS * 4 + QB4;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  int* pt_lds = reinterpret_cast<int*>(smem + RG::MAIN);
+  float* qs = reinterpret_cast<float*>(smem + RG::MAIN + RG::PT_CAP * 4);
+  T* qbt = reinterpret_cast<T*>(smem + RG::MAIN + RG::PT_CAP * 4 + RG::AUX_FLOATS * 4);
+
+  // ---- workgroup -> (sequence, KV head, chunk, row block); neighbours share an XCD
+  const int per = gridDim.x >> 3;
+  const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lid >= a.n_units) return;
+  const int rb = lid % a.RB;
+  int rest = lid / a.RB;
+  const int c = rest % a.n_chunks;
+  rest /= a.n_chunks;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  int Pb = a.prefix_len[b];
+  Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
+  const int L = Pb + a.N;
+  const int nst_seq = (L + RG::SK - 1) / RG::SK;  // balanced split of whole stages
+  const int c0 = (int)((long long)c * nst_seq / a.n_chunks) * RG::SK;
+  const int c1 = min((int)((long long)(c + 1) * nst_seq / a.n_chunks) * RG::SK, L);
+  const int n_st = c1 > c0 ? (c1 - c0 + RG::SK - 1) / RG::SK : 0;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lane32 = lane & 31, h = lane >> 5;
+
+  // ---- page-table slice of this chunk -> LDS
+  const int ps = a.kv.page_size;
+  int pg0 = 0;
+  if constexpr (PAGED) {
+    if (c1 > c0) {
+      pg0 = a.ps_shift >= 0 ? (c0 >> a.ps_shift) : c0 / ps;
+      const int pg1 = a.ps_shift >= 0 ? ((c1 - 1) >> a.ps_shift) : (c1 - 1) / ps;
+      for (int j = tid; j <= pg1 - pg0 && j < RG::PT_CAP; j += NT) {
+        const int pg = pg0 + j;
+        pt_lds[j] = pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1;
+      }
+    }
+    __syncthreads();
+  }
+  const long long seq_base = (long long)b * a.kv.seq_stride;
+  auto slot_of = [&](int pos) -> long long {
+    long long sl;
+    if constexpr (PAGED) {
+      const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
+      const int e = pt_lds[pg - pg0];  // the plan keeps every chunk within PT_CAP pages
+      sl = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
+    } else {
+      sl = seq_base + pos;
+    }
+    return (sl >= 0 && sl < a.kv.num_slots) ? sl : 0;  // unmapped positions read slot 0 (never visible)
+  };
+
+  // ---- copies of a stage: segment wave * LPW + j; the first SEGS / 2 segments are K rows, the rest V
+  const uint32_t ring_l =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
+  const long long slot_bytes = (long long)a.Hkv * RG::ROWB;
+  const bool wave_v = wave * LPW >= RG::SEGS / 2;
+  const char* tg = reinterpret_cast<const char*>(wave_v ? a.kv.v : a.kv.k) + (long long)g * RG::ROWB;
+  const int seg0 = (wave * LPW) % (RG::SEGS / 2);
+  // lane's row of copy j and its swizzled 16-byte column (recomputed per copy: few registers)
+  auto drow = [&](int j) { return (seg0 + j) * RG::RPS + lane / RG::CPR; };
+  auto dcol = [&](int j) { return ((lane % RG::CPR) ^ swz<T, D>(drow(j))) * 16; };
+  auto issue = [&](int i) {
+    const int key0 = c0 + i * RG::SK;
+    const uint32_t ld = ring_l + (uint32_t)((i % RG::NS) * RG::STAGE + (wave_v ? RG::TILE : 0) + seg0 * 1024);
+    if (!PAGED && key0 + RG::SK <= c1 && seq_base + key0 + RG::SK <= a.kv.num_slots) {
+      const char* bt = tg + (seq_base + key0) * slot_bytes;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) dma16_sbase(ld + j * 1024, (uint32_t)(drow(j) * slot_bytes) + dcol(j), bt);
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int pos = key0 + drow(j);
+        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < c1 ? pos : c0) * slot_bytes + dcol(j));
+      }
+    }
+  };
+  for (int i = 0; i < RG::PD && i < n_st; ++i) issue(i);
+
+  // ---- this wave's query tile (B operand of S^T = K Q^T): lane column = query row
+  bf16x8 qf[QN];
+  const int row = (rb * NW + wave) * 32 + lane32;
+  const bool row_ok = row < a.R;
+  const int t_node = row_ok ? row / a.G : a.N - 1;
+  {
+    const int j = row_ok ? row % a.G : 0;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + ((long long)(b * a.N + t_node) * a.Hq + g * a.G + j) * D;
+#pragma unroll
+    for (int ks = 0; ks < QN; ++ks) {
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * h);
+      qf[ks] = row_ok ? x : bf16x8{};
+    }
+  }
+
+  // ---- score operand: scale * qbar_g split into bf16 hi + mid + lo (B columns 0..2)
+  const bool wg_scores = a.do_scores && c0 < Pb;
+  if (wg_scores) {
+    if (a.prep_qbar) {
+      for (int d = tid; d < D; d += NT) {
+        const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
+        float acc = 0.f;
+        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];
+        qs[d] = acc;
+      }
+    } else {
+      constexpr int NP = NT / D;
+      const int d = tid % D, part = tid / D;
+      const int npairs = a.n_score_rows * a.G;
+      float acc = 0.f;
+      for (int i = part; i < npairs; i += NP) {
+        const int t = a.score_rows[i / a.G], j = i % a.G;
+        acc += (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + d];
+      }
+      qs[D + part * D + d] = acc;
+      __syncthreads();
+      if (tid < D) {
+        float sacc = 0.f;
+        for (int p = 0; p < NP; ++p) sacc += qs[D + p * D + tid];
+        qs[tid] = sacc;
+      }
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += NT) {
+      const float x = qs[d] * a.scale;
+      const bf16 hi = (bf16)x;
+      const float r1 = x - (float)hi;
+      const bf16 mid = (bf16)r1;
+      qbt[d] = hi;
+      qbt[D + d] = mid;
+      qbt[2 * D + d] = (bf16)(r1 - (float)mid);
+      qbt[3 * D + d] = (bf16)0.f;
+    }
+    __syncthreads();
+  }
+
+  // ---- ancestor bitset of this lane's node (tree, chunk reaching the verify tokens)
+  uint32_t anc[kAncWords] = {};
+  if (a.tree && c1 > Pb) {
+#pragma unroll
+    for (int w = 0; w < kAncWords; ++w) {
+      anc[w] = a.ws_anc[((long long)b * a.N + t_node) * kAncWords + w];
+      asm volatile("" ::"v"(anc[w]));  // wait for the load here, not inside the loop
+    }
+  }
+
+  // ---- per-lane LDS offsets of the operand reads inside a 32-key block
+  int koff[QN];
+#pragma unroll
+  for (int kr = 0; kr < QN; ++kr) koff[kr] = tile_off<T, D>(lane32, 2 * kr + h);
+  const int e4 = (lane & 15) >> 2, cq = lane & 3, dh = (lane >> 4) & 1;
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+      voff[db][hl] = tile_off<T, D>(4 * h + e4 + 8 * hl, 4 * db + 2 * dh + (cq >> 1)) + (cq & 1) * 8;
+  const int qb_row = lane32 < 3 ? lane32 : 3;
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = kNegInf, l = 0.f;
+  float* sdst = a.ws_s + ((long long)b * a.Hkv + g) * a.s_stride;
+
+  for (int i = 0; i < n_st; ++i) {
+    // stage i has landed once only the copies of later stages can be outstanding
+    const int after = min(RG::PD - 1, n_st - 1 - i);
+    if (after >= 2) wait_vm_lgkm0<2 * LPW>();
+    else if (after == 1) wait_vm_lgkm0<LPW>();
+    else wait_vm_lgkm0<0>();
+    barrier_only();
+    // the buffer of stage i + PD was last read in iteration i - 1, which every wave has finished
+    if (i + RG::PD < n_st) issue(i + RG::PD);
+    const char* Kt = smem + (i % RG::NS) * RG::STAGE;
+    const char* Vt = Kt + RG::TILE;
+
+    f32x16 sb[RG::NB];
+#pragma unroll
+    for (int kb = 0; kb < RG::NB; ++kb) {
+      const int kb0 = c0 + 32 * (i * RG::NB + kb);
+      if (kb0 >= c1) break;
+      const int jblk = kb0 >> 5;
+      const bool do_score = wg_scores && kb0 < Pb && (jblk % a.RB) == rb && ((jblk / a.RB) % NW) == wave;
+      const char* Kb = Kt + kb * 32 * RG::ROWB;
+      bf16x8 ka[QN];
+#pragma unroll
+      for (int ks = 0; ks < QN; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(Kb + koff[ks]);
+      f32x16 s = f32x16{};
+      if (do_score) {
+        f32x16 sc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < QN; ++ks) {
+          s = mfma_bf16(ka[ks], qf[ks], s);
+          sc = mfma_bf16(ka[ks], *reinterpret_cast<const bf16x8*>(qbt + qb_row * D + 16 * ks + 8 * h), sc);
+        }
+        // columns 0 + 1 + 2 summed by lanes 0 and 32, which hold keys kappa(v, h)
+        float tv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tv[v] = sc[v] + row_shl<1>(sc[v]) + row_shl<2>(sc[v]);
+        if (lane32 == 0) {  // whole block (rows are padded by 32; entries past P_b are never read)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<f32x4*>(sdst + kb0 + 8 * qd + 4 * h) =
+                f32x4{tv[4 * qd], tv[4 * qd + 1], tv[4 * qd + 2], tv[4 * qd + 3]};
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < QN; ++ks) s = mfma_bf16(ka[ks], qf[ks], s);
+      }
+      sb[kb] = s;
+    }
+
+#pragma unroll
+    for (int kb = 0; kb < RG::NB; ++kb) {
+      const int kb0 = c0 + 32 * (i * RG::NB + kb);
+      if (kb0 >= c1) break;
+      f32x16& s = sb[kb];
+      // mask (blocks reaching the verify tokens): visible iff j < P_b or j - P_b is an ancestor-or-self
+      if (kb0 + 32 > Pb) {
+        if (a.tree) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int an = kb0 + kappa(v, h) - Pb;
+            uint32_t word = 0;
+#pragma unroll
+            for (int w = 0; w < kAncWords; ++w) word = ((an >> 5) == w) ? anc[w] : word;
+            const bool vis = an < 0 || ((word >> (an & 31)) & 1u);
+            s[v] = vis ? s[v] : kNegInf;
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[v] = (kb0 + kappa(v, h) - Pb <= t_node) ? s[v] : kNegInf;
+        }
+      }
+      // online softmax, log2 domain, lazy rescale
+      float mx = s[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+      mx = half_max(mx) * a.scale_log2;
+      const bool grew = mx > m + kRescaleSlack;
+      if (__any(grew)) {
+        const float mn = grew ? mx : m;
+        const float alpha = grew ? fast_exp2(m - mn) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m = mn;
+      }
+      const float mneg = m == kNegInf ? 0.f : -m;
+      float psum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, mneg));
+        s[v] = p;
+        psum += p;
+      }
+      l += psum;
+      // O^T += V^T P^T
+      const char* Vb = Vt + kb * 32 * RG::ROWB;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        bf16x8 pb;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pb[u] = (bf16)s[8 * jj + u];
+        const char* Vj = Vb + jj * 16 * RG::ROWB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x4 lo = lds_read_tr16(reinterpret_cast<const T*>(Vj + voff[db][0]));
+          const bf16x4 hi = lds_read_tr16(reinterpret_cast<const T*>(Vj + voff[db][1]));
+          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = mfma_bf16(va, pb, o[db]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: this wave's rows are its own -> (m, l, o) partials straight to the workspace
+  wait_vm_lgkm0<0>();
+  const float lt = half_sum(l);
+  if (row_ok) {
+    const long long rec = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks + c;
+    float* dst = a.ws_o + rec * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * qd + 4 * h) =
+            f32x4{o[db][4 * qd], o[db][4 * qd + 1], o[db][4 * qd + 2], o[db][4 * qd + 3]};
+    if (h == 0) a.ws_ml[rec] = f32x2{m, lt};
+  }
+}
+
 __device__ __forceinline__ float block_reduce_max(float x, float* red) {
   x = wave_max(x);
   __syncthreads();
@@ -1065,7 +1394,7 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
     if (i >= Pb) return;
     float s = 0.f;
 #pragma unroll 8
-    for (int g = 0; g < a.Hkv; ++g) s += a.ws_s[((long long)b * a.Hkv + g) * a.P_max + i];
+    for (int g = 0; g < a.Hkv; ++g) s += a.ws_s[((long long)b * a.Hkv + g) * a.s_stride + i];
     a.scores[i0] = s;
   }
 }
@@ -1151,6 +1480,7 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   p.qsplit = p.prep_qbar ? (n_score_rows * p.G + kQbarPairs - 1) / kQbarPairs : 0;
   p.prep = p.prep_qbar || tree;
   p.stream = dtype == SV_BF16 && p.R <= 64;
+  p.treek = dtype == SV_BF16 && p.R > 64;
   if (p.stream) {
     // streaming kernel: waves split the keys of one (sequence, KV head) chunk
     p.RT = p.R <= 32 ? 1 : 2;
@@ -1177,7 +1507,15 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
     p.n_wg = (int)((units * p.n_chunks + 7) / 8 * 8);
   }
   const int rtiles = (p.R + 31) / 32;
-  if (!p.stream) {
+  if (p.treek) {
+    // tree kernel: kTreeWaves waves, one 32-row tile each
+    p.RT = 1;
+    p.WR = kTreeWaves;
+    p.WK = 1;
+    p.rows_per_block = 32 * kTreeWaves;
+    p.RB = (p.R + p.rows_per_block - 1) / p.rows_per_block;
+    p.Rpad = p.RB * p.rows_per_block;
+  } else if (!p.stream) {
     if (rtiles <= 1) { p.RT = 1; p.WR = 1; }
     else if (rtiles <= 2) { p.RT = 2; p.WR = 1; }
     else if (rtiles <= 4) { p.RT = 2; p.WR = 2; }
@@ -1192,27 +1530,29 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   // one resident workgroup per CU (two for the smaller bf16, D = 64 ring)
   const int occ = (dtype == SV_BF16 && D == 64) ? 2 : 1;
   const long long units = (long long)B * Hkv * p.RB;
-  const long long target = 256LL * occ;
-  long long want = (target + units / 2) / units;
-  if (want < 1) want = 1;
-  long long chunk = Lmax / want / SK * SK;
-  if (chunk < SK) chunk = SK;
-  if (chunk > 16320) chunk = 16320;
-  if ((Lmax + chunk - 1) / chunk > kMaxChunks) chunk = ((Lmax + kMaxChunks - 1) / kMaxChunks + SK - 1) / SK * SK;
-  if (page_size > 0) {  // a chunk's page-table slice must fit the LDS copy (Ring::PT_CAP entries)
-    const long long cap = (long long)(Ring<float, 64>::PT_CAP - 2) * page_size / SK * SK;
-    if (chunk > cap) chunk = cap < SK ? SK : cap;
-  }
   if (!p.stream) {
-    p.chunk = (int)chunk;
-    p.n_chunks = (int)((Lmax + chunk - 1) / chunk);
-    long long n_units = units * p.n_chunks;
-    p.n_wg = (int)((n_units + 7) / 8 * 8);
+    // chunks of whole stages, balanced over the longest sequence; about one
+    // wave of workgroups over the 256 CUs (occ per CU)
+    const long long nst = (Lmax + SK - 1) / SK;
+    long long nc = (256LL * occ + units / 2) / units;
+    const long long max_st = 4096 / SK;  // chunks of at most 4096 keys: mixed-length batches stay balanced
+    if (nc < (nst + max_st - 1) / max_st) nc = (nst + max_st - 1) / max_st;
+    if (nc > nst) nc = nst;
+    if (nc < 1) nc = 1;
+    if (page_size > 0) {  // a chunk's page-table slice must fit the LDS copy (Ring::PT_CAP entries)
+      const long long cap_st = (long long)(Ring<float, 64>::PT_CAP - 2) * page_size / SK - 1;
+      const long long need = (nst + (cap_st > 0 ? cap_st : 1) - 1) / (cap_st > 0 ? cap_st : 1);
+      if (nc < need) nc = need;
+    }
+    if (nc > kMaxChunks) nc = kMaxChunks;
+    p.n_chunks = (int)nc;
+    p.chunk = (int)(((nst + nc - 1) / nc) * SK);  // longest chunk, in keys
+    p.n_wg = (int)((units * p.n_chunks + 7) / 8 * 8);
   }
   size_t off = 0;
   p.off_o = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * D * 4);
   p.off_ml = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * 8);
-  p.off_s = off; off = align_up(off + (p.scores ? (size_t)B * Hkv * P_max * 4 : 0));
+  p.off_s = off; off = align_up(off + (p.scores ? (size_t)B * Hkv * ((size_t)P_max + 32) * 4 : 0));
   p.off_qbar = off; off = align_up(off + (p.prep_qbar ? (size_t)B * Hkv * p.qsplit * D * 4 : 0));
   p.off_anc = off; off = align_up(off + (tree ? (size_t)B * N * kAncWords * 4 : 0));
   p.bytes = off;
@@ -1247,6 +1587,20 @@ static void launch_stream(const VerifyPlan& p, const VerifyArgs& a, hipStream_t 
   else launch_stream2<D, RT, false>(p, a, st, ev0, ev1);
 }
 
+template <int D, bool PAGED>
+static void launch_tree2(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL((verify_tree<D, PAGED>), dim3(p.n_wg), dim3(64 * kTreeWaves), 0, st, (hipEvent_t)ev0,
+                          (hipEvent_t)ev1, 0, a);
+  else
+    hipLaunchKernelGGL((verify_tree<D, PAGED>), dim3(p.n_wg), dim3(64 * kTreeWaves), 0, st, a);
+}
+template <int D>
+static void launch_tree(const VerifyPlan& p, const VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
+  if (a.kv.page_table) launch_tree2<D, true>(p, a, st, ev0, ev1);
+  else launch_tree2<D, false>(p, a, st, ev0, ev1);
+}
+
 template <typename T, int D>
 static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void* ev0, void* ev1) {
   if (p.prep) {
@@ -1258,9 +1612,11 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
     if (p.stream) {
       if (p.RT == 1) launch_stream<D, 1>(p, a, st, ev0, ev1);
       else launch_stream<D, 2>(p, a, st, ev0, ev1);
+    } else if (p.treek) {
+      launch_tree<D>(p, a, st, ev0, ev1);
     }
   }
-  if (p.stream) {
+  if (p.stream || p.treek) {
   } else if (p.RT == 1 && p.WR == 1) launch_main<T, D, 1, 1>(p, a, st, ev0, ev1);
   else if (p.RT == 2 && p.WR == 1) launch_main<T, D, 2, 1>(p, a, st, ev0, ev1);
   else if (p.RT == 2 && p.WR == 2) launch_main<T, D, 2, 2>(p, a, st, ev0, ev1);
@@ -1289,8 +1645,9 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
   a.scores = scores;
   a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.R = p.R; a.RB = p.RB; a.Rpad = p.Rpad;
   a.P_max = p.P_max; a.chunk = p.chunk; a.n_chunks = p.n_chunks;
+  a.s_stride = p.P_max + 32;
   a.n_units = p.B * p.Hkv * p.RB * p.n_chunks;
-  a.all_chunks = p.stream ? 1 : 0;
+  a.all_chunks = 1;  // both main kernels write a partial for every chunk
   a.ps_shift = -1;
   if (kv.page_table && kv.page_size > 0 && (kv.page_size & (kv.page_size - 1)) == 0) {
     a.ps_shift = 0;
