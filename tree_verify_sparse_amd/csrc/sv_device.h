@@ -46,15 +46,56 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
 
 __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+// Wave-wide reductions on DPP (row shifts by 1, 2, 4, 8 inside each row of
+// 16 lanes, then the broadcasts of lane 15 into rows 1 and 3 and of lane 31
+// into rows 2 and 3): lane 63 ends with the reduction of all 64 lanes, which
+// is then broadcast.  No LDS round trips, unlike the shuffles.  Lanes a shift
+// reads from outside the row contribute the identity `id`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float id, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t id, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWS, 0xf, false);
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T x, T id, Op op) {
+  if constexpr (sizeof(T) == 4 && __is_same(T, float)) {
+    x = op(x, dpp_f<0x111, 0xf>(id, x));
+    x = op(x, dpp_f<0x112, 0xf>(id, x));
+    x = op(x, dpp_f<0x114, 0xf>(id, x));
+    x = op(x, dpp_f<0x118, 0xf>(id, x));
+    x = op(x, dpp_f<0x142, 0xa>(id, x));
+    x = op(x, dpp_f<0x143, 0xc>(id, x));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  } else {
+    x = op(x, dpp_u<0x111, 0xf>(id, x));
+    x = op(x, dpp_u<0x112, 0xf>(id, x));
+    x = op(x, dpp_u<0x114, 0xf>(id, x));
+    x = op(x, dpp_u<0x118, 0xf>(id, x));
+    x = op(x, dpp_u<0x142, 0xa>(id, x));
+    x = op(x, dpp_u<0x143, 0xc>(id, x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  }
+}
+__device__ __forceinline__ float wave_max(float x) {  // NaN lanes are skipped (fmaxf)
+  return wave_reduce(x, -__builtin_inff(), [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_min(float x) {  // NaN lanes are skipped (fminf)
+  return wave_reduce(x, __builtin_inff(), [](float a, float b) { return fminf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_reduce(x, 0.f, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return wave_reduce(x, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce(x, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return wave_reduce(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 // 2^x on the transcendental unit (2^-inf = 0).

@@ -40,6 +40,9 @@ constexpr int kRegRound = kTopkThreads * 64;  // rows up to this length stay in 
 constexpr int kBins = 2048;
 constexpr int kCand = 2048;                    // threshold-bin entries held in LDS
 constexpr int kRankMax = 256;                  // bins up to this size are ranked pairwise
+constexpr int kCandCap = 8192;                 // compacted candidate entries held in LDS
+constexpr int kCandWave = kCandCap / kTopkWaves;  // each wave's region of them
+constexpr int kMaskWords = 4096;               // selection bitmap of the candidate path (rows <= 131072)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -78,14 +81,75 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* sh, ui
   return before + inc - x;
 }
 
+// Exclusive scan of one value per thread over the workgroup with a single
+// barrier; `slots` (>= kTopkWaves words) must not be reused before the next
+// barrier of the caller.
+__device__ __forceinline__ uint32_t block_excl_scan1(uint32_t x, uint32_t* slots, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(x);
+  if (lane == 63) slots[w] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int v = 0; v < kTopkWaves; ++v) {
+    const uint32_t c = slots[v];
+    before += v < w ? c : 0u;
+    tot += c;
+  }
+  *total = tot;
+  return before + inc - x;
+}
+
 struct TopkShared {
   int32_t stage[kRegRound / 32];  // one round's selection bitmap, in index order
   uint32_t hist[kBins];
   uint32_t cand_key[kCand];
   int32_t cand_idx[kCand];
-  uint32_t sh[32];
-  float fsh[2 * kTopkWaves];
+  float cval[kCandCap + kTopkThreads];  // candidate path: compacted (value, index), per-wave
+  int32_t cidx[kCandCap + kTopkThreads];  // regions, then one discard slot per thread
+  uint32_t mask[kMaskWords];      // candidate path: selection bitmap over the row
+  uint32_t sh[64];
+  float fsh[2 * kTopkWaves + 8];
 };
+
+// Wave-level suffix search over hist[0, NB) (NB a multiple of 64, the whole
+// wave active): the bin holding the kk-th largest entry.  Returns it, with the
+// entries in higher bins in *above and those in it in *inbin; -1 when the
+// histogram holds fewer than kk entries.  Lane l reads bins NB-1-BPL*l down to
+// NB-BPL*(l+1); a lane-order scan of their sums is a count from the top.
+template <int NB>
+__device__ __forceinline__ int wave_threshold_bin(const uint32_t* hist, uint32_t kk, uint32_t* above,
+                                                  uint32_t* inbin) {
+  constexpr int BPL = NB / 64;
+  const int lane = threadIdx.x & 63;
+  uint32_t c[BPL], sum = 0;
+#pragma unroll
+  for (int q = 0; q < BPL; ++q) {
+    c[q] = hist[NB - 1 - BPL * lane - q];
+    sum += c[q];
+  }
+  const uint32_t inc = wave_incl_scan(sum);
+  const uint64_t m = __ballot(inc >= kk);
+  if (m == 0) return -1;
+  const int l0 = __builtin_ctzll(m);
+  int bin = -1;
+  uint32_t ab = 0, ib = 0;
+  if (lane == l0) {
+    uint32_t a = inc - sum;
+#pragma unroll
+    for (int q = 0; q < BPL; ++q) {
+      if (bin < 0 && a + c[q] >= kk) {
+        bin = NB - 1 - BPL * lane - q;
+        ab = a;
+        ib = c[q];
+      }
+      a += c[q];
+    }
+  }
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, l0);
+  *inbin = (uint32_t)__builtin_amdgcn_readlane((int)ib, l0);
+  return __builtin_amdgcn_readlane(bin, l0);
+}
 
 // Suffix search over hist[0, kBins): the bin holding the kk-th largest entry
 // (kk >= 1); sets sh[18] = bin, sh[19] = entries in higher bins, sh[20] =
@@ -148,6 +212,89 @@ __device__ __forceinline__ uint32_t radix_select(TopkShared& S, uint32_t kmin, u
   return prefix + kmin;
 }
 
+// Rank cut among the C entries of S.cand_key / S.cand_idx (C <= kRankMax): the
+// entry beaten by exactly krem - 1 others (a larger key, or an equal key at a
+// lower index) is the last kept one.  Returns its key; *i_tie gets its index.
+__device__ __forceinline__ uint32_t rank_cut(TopkShared& S, uint32_t C, uint32_t krem, int* i_tie) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kRankMax; i += kTopkThreads) S.hist[i] = 0;
+  __syncthreads();
+  constexpr int PARTS = kTopkThreads / kRankMax, SPANR = kRankMax / PARTS;
+  const int j = tid % kRankMax, part = tid / kRankMax;
+  if (j < (int)C) {
+    const uint32_t kj = S.cand_key[j];
+    const int ij = S.cand_idx[j];
+    uint32_t rank = 0;
+    const int i1 = min((int)C, part * SPANR + SPANR);
+    int i = part * SPANR;
+    for (; i + 8 <= i1; i += 8) {
+      uint32_t ki[8];
+      int ii[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ki[u] = S.cand_key[i + u];
+        ii[u] = S.cand_idx[i + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rank += (ki[u] > kj || (ki[u] == kj && ii[u] < ij)) ? 1u : 0u;
+    }
+    for (; i < i1; ++i) {
+      const uint32_t ki = S.cand_key[i];
+      rank += (ki > kj || (ki == kj && S.cand_idx[i] < ij)) ? 1u : 0u;
+    }
+    atomicAdd(&S.hist[j], rank);
+  }
+  __syncthreads();
+  if (tid < (int)C && S.hist[tid] == krem - 1) {
+    S.sh[22] = S.cand_key[tid];
+    S.sh[23] = (uint32_t)S.cand_idx[tid];
+  }
+  __syncthreads();
+  *i_tie = (int)S.sh[23];
+  return S.sh[22];
+}
+
+// Radix cut over the (order key, index) pairs that for_each(f) passes to
+// f(key, idx): the kk-th largest key (kk >= 1, at most the number of pairs),
+// and in *i_tie the index of the last kept pair equal to it (the need-th
+// smallest index among the pairs with that key).
+template <typename F>
+__device__ __forceinline__ uint32_t radix_cut(TopkShared& S, uint32_t kk, F&& for_each, int* i_tie) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for_each([&](uint32_t key, int) {
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  });
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    S.fsh[wave] = __uint_as_float(kmin);
+    S.fsh[kTopkWaves + wave] = __uint_as_float(kmax);
+  }
+  __syncthreads();
+  kmin = __float_as_uint(S.fsh[0]);
+  kmax = __float_as_uint(S.fsh[kTopkWaves]);
+  for (int w = 1; w < kTopkWaves; ++w) {
+    kmin = min(kmin, __float_as_uint(S.fsh[w]));
+    kmax = max(kmax, __float_as_uint(S.fsh[kTopkWaves + w]));
+  }
+  __syncthreads();
+  uint32_t need;
+  const uint32_t tau = radix_select(S, kmin, kmax, kk, [&](auto&& add) {
+    for_each([&](uint32_t key, int) { add(key); });
+  }, &need);
+  // indices are distinct: the need-th smallest index is the need-th largest ~index
+  uint32_t unused;
+  const uint32_t nidx = radix_select(S, 0u, 0xffffffffu, need, [&](auto&& add) {
+    for_each([&](uint32_t key, int idx) {
+      if (key == tau) add(~(uint32_t)idx);
+    });
+  }, &unused);
+  *i_tie = (int)~nidx;
+  return tau;
+}
+
 // NR > 0: the row (at most NR rounds) is held in registers across passes;
 // NR == 0: every pass streams the row from memory.  A round is
 // kTopkThreads * PL consecutive entries; wave w loads the span
@@ -186,11 +333,17 @@ __device__ __forceinline__ void topk_row(TopkShared& S, const float* __restrict_
 #pragma unroll
       for (int r = 0; r < NR; ++r)
         if (r < nrounds) f(r, xr[r]);
-    } else {
+    } else {  // two buffers: round r + 1 is in flight while round r is processed
+      float xb[PL];
+      if (nrounds > 0) load(0, xr[0]);
 #pragma unroll 1
-      for (int r = 0; r < nrounds; ++r) {
-        load(r, xr[0]);
+      for (int r = 0; r < nrounds; r += 2) {
+        if (r + 1 < nrounds) load(r + 1, xb);
         f(r, xr[0]);
+        if (r + 1 < nrounds) {
+          if (r + 2 < nrounds) load(r + 2, xr[0]);
+          f(r + 1, xb);
+        }
       }
     }
   };
@@ -214,12 +367,269 @@ __device__ __forceinline__ void topk_row(TopkShared& S, const float* __restrict_
     for (int j = 0; j < WPT; ++j) wv[j] = bits[tid * WPT + j];
   };
 
-  // ---- pass 1: range
+  // ---- candidate path (k <= kCandCap / 2, rows up to kMaskWords * 32).
+  // A strided sample places a band [t_lo, t_hi] that should hold the k-th
+  // largest entry (a little more than k entries of the row above t_lo, a
+  // little less than k above t_hi).  Rows longer than kCandCap keep only their
+  // entries >= t_lo (compacted into LDS); shorter rows keep every entry.  The
+  // cut then bins the kept entries inside the band (entries above t_hi are
+  // only counted), ranks the threshold bin, and the emit sets the kept
+  // entries' bits in a bitmap over the row.  Whenever an estimate misses (too
+  // few or too many kept entries, the cut outside the band, a crowded bin) a
+  // slower exact step takes over: a radix cut over the kept entries, or the
+  // full-row path below.  The compaction predicate is monotone in the value,
+  // so once at least k entries are kept, the k largest and every entry tied
+  // with the k-th are among them.  Single waves take the small sequential
+  // steps (band bins, threshold bin, ranking) so the workgroup meets few
+  // barriers.
+  const bool cand = k <= kCandCap / 2 && P <= kMaskWords * 32;
+  const bool compact = cand && P > kCandCap;
+  constexpr int SPT = NR > 0 ? 2 : 8;           // sampled entries per thread (more for longer rows)
+  constexpr int kSample = SPT * kTopkThreads;
+  float smp[SPT];
+  if (cand) {  // issued before the row, so they return first
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) smp[u] = s[(int)((long long)(SPT * tid + u) * P / kSample)];
+  }
   if constexpr (NR > 0) {
 #pragma unroll
     for (int r = 0; r < NR; ++r)
       if (r < nrounds) load(r, xr[r]);
   }
+  if (cand) {
+    const int nwords = (P + 31) >> 5;
+    for (int i = tid; i < kBins; i += kTopkThreads) S.hist[i] = 0;
+    for (int j = tid; j < nwords; j += kTopkThreads) S.mask[j] = 0;
+    if (tid == 0) S.sh[24] = 0;
+    // sample band: the sample's range, 256 value bins over it, then wave 0
+    // finds the bins of the sample ranks r + 4 sqrt(r) + 4 (t_lo = that bin's
+    // lower edge) and r - 4 sqrt(r) (t_hi = that bin's upper edge), where
+    // r = k kSample / P is where the k-th largest entry is expected among the
+    // samples (about Poisson-distributed, so 4 sqrt(r) is four deviations)
+    uint32_t* sb = S.cand_key;  // 256 bins
+    if (tid < 256) sb[tid] = 0;
+    float a0 = __builtin_inff(), a1 = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      a0 = fminf(a0, smp[u]);  // NaN skipped
+      a1 = fmaxf(a1, smp[u]);
+    }
+    a0 = wave_min(a0);
+    a1 = wave_max(a1);
+    if (lane == 0) {
+      S.fsh[wave] = a0;
+      S.fsh[kTopkWaves + wave] = a1;
+    }
+    __syncthreads();
+    float smin = S.fsh[0], smax = S.fsh[kTopkWaves];
+#pragma unroll
+    for (int w = 1; w < kTopkWaves; ++w) {
+      smin = fminf(smin, S.fsh[w]);
+      smax = fmaxf(smax, S.fsh[kTopkWaves + w]);
+    }
+    const float sw = smax - smin;
+    const float sbs = 256.f / sw;
+    const bool sok = sw > 0.f && sw < __builtin_inff() && sbs < __builtin_inff();
+    if (sok) {
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const float b = (smp[u] - smin) * sbs;
+        if (smp[u] == smp[u]) atomicAdd(&sb[b < 255.f ? (int)b : 255], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      float tl = smin, th = smax;
+      if (sok) {
+        const float rk = (float)k * (float)kSample / (float)P;  // expected sample rank of the cut
+        const float dev = 4.f * __builtin_sqrtf(rk);
+        const uint32_t want_lo = (uint32_t)fminf(rk + dev + 4.f, (float)kSample);
+        const uint32_t want_hi = (uint32_t)fmaxf(rk - dev, 1.f);
+        uint32_t ab, ib;
+        const int bh = wave_threshold_bin<256>(sb, want_hi, &ab, &ib);
+        const int bl = wave_threshold_bin<256>(sb, want_lo, &ab, &ib);
+        tl = smin + sw * ((float)(bl > 0 ? bl : 0) * (1.f / 256.f));
+        th = bh >= 0 ? fminf(smin + sw * ((float)(bh + 1) * (1.f / 256.f)), smax) : smax;
+      }
+      if (lane == 0) {
+        S.fsh[2 * kTopkWaves] = tl;
+        S.fsh[2 * kTopkWaves + 1] = th;
+      }
+    }
+    __syncthreads();
+    const float t_lo = S.fsh[2 * kTopkWaves], t_hi = S.fsh[2 * kTopkWaves + 1];
+
+    // compaction without branches.  Long rows: wave w appends its entries
+    // >= t_lo to its region [w * kCandWave, (w + 1) * kCandWave) at ballot
+    // positions.  Short rows: every entry sits at its own index, so region w
+    // holds entries [w * kCandWave, (w + 1) * kCandWave).  Lanes with nothing
+    // to keep write their discard slot.
+    uint32_t wbase = 0;  // wave-uniform
+    const int discard = kCandCap + tid;
+    if (compact) {
+      rounds([&](int r, const float(&x)[PL]) {
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          const bool pr = x[e] >= t_lo;  // NaN padding: no
+          const uint64_t m = __ballot(pr);
+          const uint32_t pos =
+              wbase + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          const int slot = (pr && pos < (uint32_t)kCandWave) ? wave * kCandWave + (int)pos : discard;
+          S.cval[slot] = x[e];
+          S.cidx[slot] = entry(r, e >> 2, e & 3);
+          wbase += (uint32_t)__builtin_popcountll(m);
+        }
+      });
+    } else {
+      rounds([&](int r, const float(&x)[PL]) {
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          const int i = entry(r, e >> 2, e & 3);
+          const int slot = i < P ? i : discard;
+          S.cval[slot] = x[e];
+          S.cidx[slot] = i;
+        }
+      });
+    }
+    if (lane == 0) S.sh[wave] = wbase;
+    __syncthreads();
+    uint32_t c_total = 0, nw[kTopkWaves];
+    bool fits = true;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+      nw[w] = compact ? S.sh[w] : (uint32_t)min(max(P - w * kCandWave, 0), kCandWave);
+      c_total += nw[w];
+      fits = fits && nw[w] <= (uint32_t)kCandWave;
+    }
+
+    if (fits && c_total >= (uint32_t)k) {
+      // thread t holds the kept entries of slots t + kTopkThreads * u (u < CPT)
+      constexpr int CPT = kCandCap / kTopkThreads;
+      static_assert(kCandWave == 2 * kTopkThreads, "two slots of each region per thread");
+      bool own[CPT];
+      float cv[CPT];
+      int ci[CPT];
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {  // slot u: region u / 2, offset tid + kTopkThreads * (u % 2)
+        const int j = tid + kTopkThreads * u;
+        own[u] = (uint32_t)(tid + kTopkThreads * (u & 1)) < nw[u >> 1];
+        cv[u] = S.cval[j];
+        ci[u] = S.cidx[j];
+      }
+      // band histogram: kept entries inside [t_lo, t_hi] binned, those above t_hi counted
+      constexpr int kBand = 512;  // value bins over the band
+      const float bw = t_hi - t_lo;
+      const float bbs = (float)kBand / bw;
+      const bool band = bw > 0.f && bw < __builtin_inff() && bbs < __builtin_inff();
+      auto in_band = [&](float v) { return band && v >= t_lo && v <= t_hi; };  // NaN: no
+      auto bbin = [&](float v) {
+        const float t = (v - t_lo) * bbs;
+        return t < (float)(kBand - 1) ? (int)t : kBand - 1;
+      };
+      uint32_t above = 0;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        above += (own[u] && cv[u] > t_hi) ? 1u : 0u;
+        if (own[u] && in_band(cv[u])) atomicAdd(&S.hist[bbin(cv[u])], 1u);
+      }
+      above = wave_sum_u32(above);
+      if (lane == 0) S.sh[8 + wave] = above;
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t A = 0;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) A += S.sh[8 + w];
+        uint32_t ab = 0, ib = 0;
+        const int beta = (band && A < (uint32_t)k) ? wave_threshold_bin<kBand>(S.hist, (uint32_t)k - A, &ab, &ib) : -1;
+        if (lane == 0) {
+          S.sh[18] = (uint32_t)beta;
+          S.sh[19] = A + ab;
+          S.sh[20] = ib;
+        }
+      }
+      __syncthreads();
+      const int beta = (int)S.sh[18];
+      const uint32_t C = S.sh[20];
+      const uint32_t krem = (uint32_t)k - S.sh[19];
+      uint32_t tau_c = 0;
+      int tie_c = -1;
+      if (beta >= 0 && C <= (uint32_t)kRankMax) {
+        // the threshold bin's entries, ranked by (key descending, index ascending)
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+          if (own[u] && in_band(cv[u]) && bbin(cv[u]) == beta) {
+            const uint32_t at = atomicAdd(&S.sh[24], 1u);
+            S.cand_key[at] = order_key(cv[u]);
+            S.cand_idx[at] = ci[u];
+          }
+        }
+        __syncthreads();
+        if (C <= 64u) {
+          if (wave == 0) {  // lane j ranks entry j against all C (register broadcasts)
+            const bool act = lane < (int)C;
+            const uint32_t kj = act ? S.cand_key[lane] : 0u;
+            const int ij = act ? S.cand_idx[lane] : 0;
+            uint32_t rank = 0;
+            for (int i = 0; i < (int)C; ++i) {
+              const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
+              const int ii = __builtin_amdgcn_readlane(ij, i);
+              rank += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+            }
+            if (act && rank == krem - 1) {
+              S.sh[22] = kj;
+              S.sh[23] = (uint32_t)ij;
+            }
+          }
+          __syncthreads();
+          tau_c = S.sh[22];
+          tie_c = (int)S.sh[23];
+        } else {
+          tau_c = rank_cut(S, C, krem, &tie_c);
+        }
+      } else {
+        tau_c = radix_cut(S, (uint32_t)k, [&](auto&& f) {
+#pragma unroll
+          for (int u = 0; u < CPT; ++u)
+            if (own[u]) f(order_key(cv[u]), ci[u]);
+        }, &tie_c);
+      }
+
+      // emit: kept entries as a bitmap over the row (zeroed above), then
+      // each thread's contiguous words -> popcount, one scan, indices in order
+      const float tf = key_value(tau_c);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const bool keep = own[u] && (cv[u] > tf || (cv[u] == tf && ci[u] <= tie_c));
+        if (keep) atomicOr(&S.mask[ci[u] >> 5], 1u << (ci[u] & 31));
+      }
+      __syncthreads();
+      const int wpt = (nwords + kTopkThreads - 1) / kTopkThreads;  // at most kMaskWords / kTopkThreads
+      uint32_t mw[kMaskWords / kTopkThreads];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kMaskWords / kTopkThreads; ++j) {
+        const int wi = tid * wpt + j;
+        mw[j] = (j < wpt && wi < nwords) ? S.mask[wi] : 0u;
+        cnt += (uint32_t)__builtin_popcount(mw[j]);
+      }
+      uint32_t tot;
+      uint32_t pos = block_excl_scan1(cnt, S.sh + 48, &tot);
+#pragma unroll
+      for (int j = 0; j < kMaskWords / kTopkThreads; ++j) {
+        uint32_t m = mw[j];
+        while (m) {
+          const int bpos = __builtin_ctz(m);
+          m &= m - 1;
+          if (pos < (uint32_t)k) out[pos] = (tid * wpt + j) * 32 + bpos;
+          ++pos;
+        }
+      }
+      return;
+    }
+    __syncthreads();  // the full-row path below rewrites LDS the candidate path read
+  }
+
+  // ---- pass 1: range
   float vmin = __builtin_inff(), vmax = -__builtin_inff();
   rounds([&](int, const float(&x)[PL]) {
 #pragma unroll
@@ -228,11 +638,8 @@ __device__ __forceinline__ void topk_row(TopkShared& S, const float* __restrict_
       vmax = fmaxf(vmax, x[e]);
     }
   });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    vmin = fminf(vmin, __shfl_xor(vmin, o));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, o));
-  }
+  vmin = wave_min(vmin);
+  vmax = wave_max(vmax);
   if (lane == 0) {
     S.fsh[wave] = vmin;
     S.fsh[kTopkWaves + wave] = vmax;
@@ -292,79 +699,13 @@ __device__ __forceinline__ void topk_row(TopkShared& S, const float* __restrict_
       });
       __syncthreads();
       if (C <= (uint32_t)kRankMax) {
-        // rank of candidate j = number of candidates beating it (larger key, or equal key at a lower index)
-        for (int i = tid; i < kRankMax; i += kTopkThreads) S.hist[i] = 0;
-        __syncthreads();
-        constexpr int PARTS = kTopkThreads / kRankMax, SPANR = kRankMax / PARTS;
-        const int j = tid % kRankMax, part = tid / kRankMax;
-        if (j < (int)C) {
-          const uint32_t kj = S.cand_key[j];
-          const int ij = S.cand_idx[j];
-          uint32_t rank = 0;
-          const int i1 = min((int)C, part * SPANR + SPANR);
-          int i = part * SPANR;
-          for (; i + 8 <= i1; i += 8) {
-            uint32_t ki[8];
-            int ii[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              ki[u] = S.cand_key[i + u];
-              ii[u] = S.cand_idx[i + u];
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) rank += (ki[u] > kj || (ki[u] == kj && ii[u] < ij)) ? 1u : 0u;
-          }
-          for (; i < i1; ++i) {
-            const uint32_t ki = S.cand_key[i];
-            rank += (ki > kj || (ki == kj && S.cand_idx[i] < ij)) ? 1u : 0u;
-          }
-          atomicAdd(&S.hist[j], rank);
-        }
-        __syncthreads();
-        if (tid < (int)C && S.hist[tid] == krem - 1) {
-          S.sh[22] = S.cand_key[tid];
-          S.sh[23] = (uint32_t)S.cand_idx[tid];
-        }
-        __syncthreads();
-        tau_key = S.sh[22];
-        i_tie = (int)S.sh[23];
+        tau_key = rank_cut(S, C, krem, &i_tie);
       } else {
-        // radix select of the krem-th largest key among the candidates, then
-        // the need-th smallest index among the candidates equal to it
-        uint32_t cmin = 0xffffffffu, cmax = 0u;
-        for (uint32_t j = tid; j < C; j += kTopkThreads) {
-          cmin = min(cmin, S.cand_key[j]);
-          cmax = max(cmax, S.cand_key[j]);
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          cmin = min(cmin, (uint32_t)__shfl_xor((int)cmin, o));
-          cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o));
-        }
-        if (lane == 0) {
-          S.fsh[wave] = __uint_as_float(cmin);
-          S.fsh[kTopkWaves + wave] = __uint_as_float(cmax);
-        }
-        __syncthreads();
-        cmin = __float_as_uint(S.fsh[0]);
-        cmax = __float_as_uint(S.fsh[kTopkWaves]);
-        for (int w = 1; w < kTopkWaves; ++w) {
-          cmin = min(cmin, __float_as_uint(S.fsh[w]));
-          cmax = max(cmax, __float_as_uint(S.fsh[kTopkWaves + w]));
-        }
-        __syncthreads();
-        uint32_t need;
-        tau_key = radix_select(S, cmin, cmax, krem, [&](auto&& add) {
-          for (uint32_t j = tid; j < C; j += kTopkThreads) add(S.cand_key[j]);
-        }, &need);
-        // indices are distinct: the need-th smallest index is the need-th largest ~index
-        const uint32_t tk = tau_key;
-        uint32_t unused;
-        const uint32_t nidx = radix_select(S, 0u, 0xffffffffu, need, [&](auto&& add) {
-          for (uint32_t j = tid; j < C; j += kTopkThreads)
-            if (S.cand_key[j] == tk) add(~(uint32_t)S.cand_idx[j]);
-        }, &unused);
-        i_tie = (int)~nidx;
+        // the krem-th largest key among the candidates, then the index of the
+        // last kept candidate equal to it
+        tau_key = radix_cut(S, krem, [&](auto&& f) {
+          for (uint32_t j = tid; j < C; j += kTopkThreads) f(S.cand_key[j], S.cand_idx[j]);
+        }, &i_tie);
       }
       have_cut = true;
     }
