@@ -182,6 +182,90 @@ def test_sparse_draft_direct(dtype, D, G, paged):
     assert (g[1] == 0).all()
 
 
+def _sparse_case(seed, dtype="bf16", paged=False):
+    Hkv = 4
+    wl = make_custom(seed=seed, B=3, Hq=4 * Hkv, Hkv=Hkv, D=128, dtype=dtype, P=[900, 300, 620], N=4,
+                     score_rows="all", k_sel=10, decode_steps=1, q_std_mult=6.0,
+                     layout="paged" if paged else "contiguous", page_size=16)
+    return wl, DevWorkload(wl)
+
+
+def _sparse_lists(rng, sizes, spans):
+    return [rng.choice(span, size, replace=False).astype(np.int32) for size, span in zip(sizes, spans)]
+
+
+def _sparse_call_and_check(wl, dw, lists, stride, max_idx, ws, what):
+    arr = np.full((len(lists), stride), -1, np.int32)
+    for b, li in enumerate(lists):
+        arr[b, : len(li)] = li
+    n = np.array([len(x) for x in lists], np.int32)
+    out = sv.sparse_draft_attn(dw.dq[0], dw.kv, i32(arr), i32(n), max_idx=max_idx, workspace=ws)
+    ref = oracle.sparse_draft_attention(wl.dq[0], wl.dtype, OKV.of(wl), lists, wl.scale, wl.Hkv)
+    check_out(as_f64(out), ref, wl.dtype, what)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sparse_workspace_garbage_and_reuse(paged):
+    """The workspace is scratch: a workspace full of garbage, and the same
+    workspace reused with other list lengths, give the same results as fresh
+    memory would."""
+    wl, dw = _sparse_case(410 + int(paged), paged=paged)
+    rng = np.random.default_rng(7)
+    ws = sv.Workspace()
+    nbytes = sv.sparse_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, 512)
+    ws.get(nbytes, "cuda")
+    for fill in ("random", 0xFF, 0x00, "random"):
+        if fill == "random":
+            ws.buf.copy_(torch.randint(0, 256, ws.buf.shape, dtype=torch.uint8, device="cuda"))
+        else:
+            ws.buf.fill_(fill)
+        for sizes in ([512, 1, 300], [65, 200, 0], [128, 64, 511]):
+            lists = _sparse_lists(rng, sizes, [904, 304, 624])
+            _sparse_call_and_check(wl, dw, lists, 512, 512, ws, f"sparse fill={fill} sizes={sizes}")
+
+
+def test_sparse_graph_replay():
+    """Captured once in a HIP graph, replayed with other index lists and list
+    lengths, with eager calls on the same workspace in between: every replay
+    matches the oracle (nothing carries over from one launch to the next)."""
+    wl, dw = _sparse_case(420)
+    rng = np.random.default_rng(9)
+    stride = 512
+    ws = sv.Workspace()
+    ws.get(sv.sparse_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, stride), "cuda")
+    idx_t = torch.full((wl.B, stride), -1, dtype=torch.int32, device="cuda")
+    n_t = torch.zeros((wl.B,), dtype=torch.int32, device="cuda")
+    q = dw.dq[0].contiguous()
+    out = torch.empty_like(q)
+    sizes0 = [300, 200, 100]
+    lists = _sparse_lists(rng, sizes0, [904, 304, 624])
+
+    def load(lists):
+        arr = np.full((wl.B, stride), -1, np.int32)
+        for b, li in enumerate(lists):
+            arr[b, : len(li)] = li
+        idx_t.copy_(torch.from_numpy(arr))
+        n_t.copy_(torch.from_numpy(np.array([len(x) for x in lists], np.int32)))
+
+    load(lists)
+    sv.sparse_draft_attn(q, dw.kv, idx_t, n_t, max_idx=stride, out=out, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.sparse_draft_attn(q, dw.kv, idx_t, n_t, max_idx=stride, out=out, workspace=ws)
+    for rep, sizes in enumerate(([300, 200, 100], [512, 7, 0], [64, 300, 450], [1, 1, 1])):
+        lists = _sparse_lists(rng, sizes, [904, 304, 624])
+        load(lists)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.sparse_draft_attention(wl.dq[0], wl.dtype, OKV.of(wl), lists, wl.scale, wl.Hkv)
+        check_out(as_f64(out), ref, wl.dtype, f"replay {rep} sizes={sizes}")
+        # an eager call on the same workspace (a new epoch) between replays
+        eager_lists = _sparse_lists(rng, [33, 44, 55], [904, 304, 624])
+        _sparse_call_and_check(wl, dw, eager_lists, stride, stride, ws, f"eager after replay {rep}")
+        torch.cuda.synchronize()
+
+
 def test_sparse_full_index_equals_dense_verify_row():
     """k = whole context: the draft output equals dense attention of the same query (N = 1 verify)."""
     wl = make_custom(seed=300, B=1, Hq=32, Hkv=8, D=128, dtype="bf16", P=4000, N=1, score_rows="all",
