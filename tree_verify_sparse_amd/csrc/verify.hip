@@ -100,6 +100,25 @@ struct VerifyArgs {
 // key offset (within a 32-key block) of accumulator element v for lane half h
 __device__ __forceinline__ int kappa(int v, int h) { return mfma_row(v, h); }
 
+// Tree visibility of a 32-key block for one node: bit j of the result is set
+// iff key kb0 + j is a prefix entry (an = kb0 + j - P_b < 0) or the verify
+// token an is an ancestor-or-self of the node (bit an of its ancestor set).
+// an0 = kb0 - P_b > -32; tokens at or past N (<= 256) have no bits, so keys
+// past the sequence end are never visible.  Two words of the set are picked
+// once per block and funnel-shifted, so each key costs one bit test.
+__device__ __forceinline__ uint32_t anc_window(const uint32_t (&anc)[kAncWords], int an0) {
+  const int w0 = an0 >> 5;  // -1 .. kAncWords - 1
+  uint32_t lo = w0 < 0 ? 0xffffffffu : 0u, hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kAncWords; ++w) {
+    lo = (w == w0) ? anc[w] : lo;
+    hi = (w == w0 + 1) ? anc[w] : hi;
+  }
+  return (uint32_t)(((((unsigned long long)hi) << 32) | lo) >> (an0 & 31));
+}
+// Visibility of lane (v, h)'s key kappa(v, h) in a block with window `win`.
+__device__ __forceinline__ bool win_vis(uint32_t win, int v, int h) { return (win >> kappa(v, h)) & 1u; }
+
 // 2-lane-shifted copies within a row of 16 lanes (DPP): lane i gets lane i + N's x (0 past the row end)
 template <int N>
 __device__ __forceinline__ float row_shl(float x) {
@@ -239,7 +258,8 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
       for (int d = tid; d < D; d += 256) {
         const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
         float acc = 0.f;
-        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];
+#pragma unroll 16
+        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];  // unrolled: the loads go out together
         qs[d] = acc;
       }
     } else {
@@ -411,16 +431,14 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
       if (kb0 + 32 > min(Pb, c1)) {
         if (a.tree) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
+          for (int rt = 0; rt < RT; ++rt) {
+            const uint32_t win = kb0 + 32 > Pb ? anc_window(anc[rt], kb0 - Pb) : 0xffffffffu;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int key = kb0 + kappa(v, h), an = key - Pb;
-              uint32_t word = 0;
-#pragma unroll
-              for (int w = 0; w < kAncWords; ++w) word = ((an >> 5) == w) ? anc[rt][w] : word;
-              const bool vis = key < c1 && (an < 0 || ((word >> (an & 31)) & 1u));
+              const bool vis = kb0 + kappa(v, h) < c1 && win_vis(win, v, h);
               s[rt][v] = vis ? s[rt][v] : kNegInf;
             }
+          }
         } else {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
@@ -752,7 +770,8 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       for (int d = tid; d < D; d += 256) {
         const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
         float acc = 0.f;
-        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];
+#pragma unroll 16
+        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];  // unrolled: the loads go out together
         qs[d] = acc;
       }
     } else {
@@ -895,16 +914,11 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
     if (key0 + 32 > Pb) {
       if (a.tree) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint32_t win = anc_window(anc[rt], key0 - Pb);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int an = key0 + kappa(v, h) - Pb;
-            uint32_t word = 0;
-#pragma unroll
-            for (int w = 0; w < kAncWords; ++w) word = ((an >> 5) == w) ? anc[rt][w] : word;
-            const bool vis = an < 0 || ((word >> (an & 31)) & 1u);
-            s[rt][v] = vis ? s[rt][v] : kNegInf;
-          }
+          for (int v = 0; v < 16; ++v) s[rt][v] = win_vis(win, v, h) ? s[rt][v] : kNegInf;
+        }
       } else {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -1133,7 +1147,8 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
       for (int d = tid; d < D; d += NT) {
         const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
         float acc = 0.f;
-        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];
+#pragma unroll 16
+        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];  // unrolled: the loads go out together
         qs[d] = acc;
       }
     } else {
@@ -1141,6 +1156,7 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
       const int d = tid % D, part = tid / D;
       const int npairs = a.n_score_rows * a.G;
       float acc = 0.f;
+#pragma unroll 4
       for (int i = part; i < npairs; i += NP) {
         const int t = a.score_rows[i / a.G], j = i % a.G;
         acc += (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + d];
@@ -1196,7 +1212,12 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   float m = kNegInf, l = 0.f;
   float* sdst = a.ws_s + ((long long)b * a.Hkv + g) * a.s_stride;
 
-  for (int i = 0; i < n_st; ++i) {
+  // Stage i: wait for its copies, start the copies of stage i + PD, then the
+  // two blocks' S^T products followed by their softmax and P V.  Stages whose
+  // keys all lie in the prefix need no mask and run a copy of the body
+  // without it (no mask code, no merges of masked and unmasked tiles).
+  auto stage = [&](int i, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     // stage i has landed once only the copies of later stages can be outstanding
     const int after = min(RG::PD - 1, n_st - 1 - i);
     if (after >= 2) wait_vm_lgkm0<2 * LPW>();
@@ -1250,17 +1271,11 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
       if (kb0 >= c1) break;
       f32x16& s = sb[kb];
       // mask (blocks reaching the verify tokens): visible iff j < P_b or j - P_b is an ancestor-or-self
-      if (kb0 + 32 > Pb) {
+      if (MASKED && kb0 + 32 > Pb) {
         if (a.tree) {
+          const uint32_t win = anc_window(anc, kb0 - Pb);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int an = kb0 + kappa(v, h) - Pb;
-            uint32_t word = 0;
-#pragma unroll
-            for (int w = 0; w < kAncWords; ++w) word = ((an >> 5) == w) ? anc[w] : word;
-            const bool vis = an < 0 || ((word >> (an & 31)) & 1u);
-            s[v] = vis ? s[v] : kNegInf;
-          }
+          for (int v = 0; v < 16; ++v) s[v] = win_vis(win, v, h) ? s[v] : kNegInf;
         } else {
 #pragma unroll
           for (int v = 0; v < 16; ++v) s[v] = (kb0 + kappa(v, h) - Pb <= t_node) ? s[v] : kNegInf;
@@ -1306,7 +1321,10 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
         }
       }
     }
-  }
+  };
+  const int n_plain = min(max((Pb - c0) / RG::SK, 0), n_st);
+  for (int i = 0; i < n_plain; ++i) stage(i, std::false_type{});
+  for (int i = n_plain; i < n_st; ++i) stage(i, std::true_type{});
 
   // ---- epilogue: this wave's rows are its own -> (m, l, o) partials straight to the workspace
   wait_vm_lgkm0<0>();
