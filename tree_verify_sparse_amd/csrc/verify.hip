@@ -1342,66 +1342,96 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   }
 }
 
-__device__ __forceinline__ float block_reduce_max(float x, float* red) {
-  x = wave_max(x);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-__device__ __forceinline__ float block_reduce_sum(float x, float* red) {
-  x = wave_sum(x);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-// Split-KV merge (log-sum-exp weights) + per-KV-head score sum.  One
-// workgroup per (sequence, KV head, query row): all chunk partials of the row
-// are read at once, spread over the threads, and reduced in a fixed order.
+// Split-KV merge (log-sum-exp weights) + per-KV-head score sum.  wpr waves
+// (1 or 4) per (sequence, KV head, query row), 4 / wpr rows per workgroup.
+// The two halves of each of the row's waves take every (2 wpr)-th chunk
+// (lane q of a half holds columns 4q..4q+3) and merge them in one pass, eight
+// chunks' (m, l, o) loads in flight per lane: each batch's max rescales the
+// running sums once.  Halves, then waves (through LDS), are combined in a
+// fixed order with their own log-sum-exp weights, so results do not depend
+// on timing.  Four waves per row when rows have many chunks (few, long
+// rows), one otherwise.  Workgroups past the row ones sum the per-head score
+// partials of 256 prefix entries each.
 constexpr int kMaxChunks = 1024;
 
+// (m, l, o) partial of a merge lane; merging two is log-sum-exp weighting
+struct MergeAcc {
+  float m, l;
+  f32x4 o;
+};
+__device__ __forceinline__ MergeAcc merge_acc(const MergeAcc& x, const MergeAcc& y) {
+  const float M = fmaxf(x.m, y.m);
+  const float wx = x.m == kNegInf ? 0.f : fast_exp2(x.m - M);
+  const float wy = y.m == kNegInf ? 0.f : fast_exp2(y.m - M);
+  return MergeAcc{M, wx * x.l + wy * y.l, wx * x.o + wy * y.o};
+}
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_row_wgs) {
+__global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_row_wgs, int wpr) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < n_row_wgs) {
-    __shared__ float wsh[kMaxChunks];
-    __shared__ float red[4];
-    __shared__ f32x4 part[256];
-    const int gr = blockIdx.x;  // (b, g, row)
+    __shared__ MergeAcc red[4][32];
+    const int lane = tid & 63, wave = tid >> 6;
+    const int sub = wave % wpr;
+    const int gr = (int)blockIdx.x * (4 / wpr) + wave / wpr;  // (b, g, row); uniform over a row's waves
+    if (gr >= a.B * a.Hkv * a.R) return;
     const int row = gr % a.R, bg = gr / a.R, g = bg % a.Hkv, b = bg / a.Hkv;
     int Pb = a.prefix_len[b];
     Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
     const int nc = a.all_chunks ? a.n_chunks : min((Pb + a.N + a.chunk - 1) / a.chunk, a.n_chunks);
     const long long rec0 = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks;
-    float mloc = kNegInf;
-    for (int c = tid; c < nc; c += 256) mloc = fmaxf(mloc, a.ws_ml[rec0 + c][0]);
-    const float M = block_reduce_max(mloc, red);
-    float lloc = 0.f;
-    for (int c = tid; c < nc; c += 256) {
-      const f32x2 ml = a.ws_ml[rec0 + c];
-      const float w = (M == kNegInf) ? 0.f : fast_exp2(ml[0] - M);
-      wsh[c] = w;
-      lloc += w * ml[1];
-    }
-    const float lsum = block_reduce_sum(lloc, red);  // (its barriers also publish wsh)
-    constexpr int Q4 = D / 4, PH = 256 / Q4;
-    const int quad = tid % Q4, ph = tid / Q4;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int c = ph; c < nc; c += PH)
-      acc += wsh[c] * *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * quad);
-    part[tid] = acc;
-    __syncthreads();
-    if (tid < Q4) {
-      f32x4 t = part[tid];
-      for (int p2 = 1; p2 < PH; ++p2) t += part[p2 * Q4 + tid];
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      const int tn = row / a.G, j = row % a.G;
-      T* dst = reinterpret_cast<T*>(a.out) + ((long long)(b * a.N + tn) * a.Hq + g * a.G + j) * D + 4 * tid;
+    static_assert(D / 4 <= 32, "one float4 column group per lane of a half");
+    const int half = lane >> 5, q = lane & 31;
+    const int qc = q < D / 4 ? q : 0;  // lanes past the row width repeat column group 0 (not stored)
+    MergeAcc acc{kNegInf, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    constexpr int BATCH = 8;
+    for (int c0 = 2 * sub + half; c0 < nc; c0 += 2 * wpr * BATCH) {
+      f32x2 ml[BATCH];
+      f32x4 ov[BATCH];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = (T)(t[e] * inv);
+      for (int u = 0; u < BATCH; ++u) {
+        const int c = c0 + 2 * wpr * u;
+        const bool ok = c < nc;
+        ml[u] = ok ? a.ws_ml[rec0 + c] : f32x2{kNegInf, 0.f};
+        ov[u] = ok ? *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * qc) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float bm = acc.m;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) bm = fmaxf(bm, ml[u][0]);
+      const float wa = acc.m == kNegInf ? 0.f : fast_exp2(acc.m - bm);
+      acc.l *= wa;
+      acc.o *= wa;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const float w = ml[u][0] == kNegInf ? 0.f : fast_exp2(ml[u][0] - bm);
+        acc.l += w * ml[u][1];
+        acc.o += w * ov[u];
+      }
+      acc.m = bm;
+    }
+    // halves: lane q of half 1 joins lane q of half 0 (same columns, other chunks)
+    {
+      MergeAcc oth;
+      oth.m = __shfl_xor(acc.m, 32);
+      oth.l = __shfl_xor(acc.l, 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oth.o[e] = __shfl_xor(acc.o[e], 32);
+      acc = half == 0 ? merge_acc(acc, oth) : merge_acc(oth, acc);
+    }
+    if (wpr > 1) {  // the row's waves share one workgroup: merge their results in wave order
+      if (half == 0) red[wave][q] = acc;
+      __syncthreads();
+      if (sub == 0) {
+        acc = red[wave][q];
+        for (int w = 1; w < wpr; ++w) acc = merge_acc(acc, red[wave + w][q]);
+      }
+    }
+    if (sub == 0 && half == 0 && q < D / 4) {
+      const float inv = acc.l > 0.f ? 1.f / acc.l : 0.f;
+      const int tn = row / a.G, j = row % a.G;
+      T* dst = reinterpret_cast<T*>(a.out) + ((long long)(b * a.N + tn) * a.Hq + g * a.G + j) * D + 4 * q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = (T)(acc.o[e] * inv);
     }
   } else {
     const long long i0 = (long long)(blockIdx.x - n_row_wgs) * 256 + tid;
@@ -1639,9 +1669,10 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
   else if (p.RT == 2 && p.WR == 1) launch_main<T, D, 2, 1>(p, a, st, ev0, ev1);
   else if (p.RT == 2 && p.WR == 2) launch_main<T, D, 2, 2>(p, a, st, ev0, ev1);
   else launch_main<T, D, 2, 4>(p, a, st, ev0, ev1);
-  const int n_row_wgs = p.B * p.Hkv * p.R;
+  const int wpr = p.n_chunks >= 16 ? 4 : 1;  // waves per merged row
+  const int n_row_wgs = (p.B * p.Hkv * p.R * wpr + 3) / 4;
   const long long n_s = p.scores ? ((long long)p.B * p.P_max + 255) / 256 : 0;
-  hipLaunchKernelGGL((verify_merge<T, D>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs);
+  hipLaunchKernelGGL((verify_merge<T, D>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
   return (int)hipGetLastError();
 }
 
