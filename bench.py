@@ -187,9 +187,13 @@ def main():
         vis += int(wl.N * Pb[b] + (depth + 1).sum())
     verify_flops = 4 * wl.Hq * wl.D * vis
 
-    mfma_bound = wl.N * (wl.Hq // wl.Hkv) >= 256  # wide trees: dense contraction
+    # the bound is the roof the kernel would hit first at full efficiency: MFMA when the
+    # verify pass's arithmetic intensity (flops per algorithmic byte) exceeds the ridge
+    # point peak_flops / peak_bytes, HBM otherwise
+    peak = BF16_MFMA_PEAK_TFS if wl.dtype == "bf16" else F32_MFMA_PEAK_TFS
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = verify_flops / verify_bytes >= ridge
     if mfma_bound:
-        peak = BF16_MFMA_PEAK_TFS if wl.dtype == "bf16" else F32_MFMA_PEAK_TFS
         achieved = verify_flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
@@ -203,6 +207,8 @@ def main():
     else:
         roof["kernel"] = "verify_main"
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    roof["flops_per_byte"] = round(verify_flops / verify_bytes, 1)
+    roof["ridge_flops_per_byte"] = round(ridge, 1)
     roof["algorithmic_bytes"] = verify_bytes
     roof["algorithmic_flops"] = verify_flops
     roof["traffic"] = _traffic(args.workload)
