@@ -655,13 +655,23 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
   float* qs = reinterpret_cast<float*>(smem + WRg::MAIN + WRg::PT_CAP * 4);
   T* qbt = reinterpret_cast<T*>(smem + WRg::MAIN + WRg::PT_CAP * 4 + WRg::AUX_FLOATS * 4);
 
-  // ---- workgroup -> (sequence, KV head, chunk); neighbouring chunks share an XCD
-  const int per = gridDim.x >> 3;
-  const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lid >= a.n_units) return;
-  const int c = lid % a.n_chunks;
-  const int bg = lid / a.n_chunks;
-  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  // ---- workgroup -> (sequence, KV head, chunk).  Batches: chunk c runs on XCD
+  // c % 8 (blockIdx % 8 picks the XCD), so every XCD gets a slice of every
+  // sequence and head whatever the lengths.  One sequence: each XCD streams
+  // whole heads (consecutive chunks), which measured slightly faster.
+  int c, g, b;
+  if (a.B > 1) {
+    c = (int)(blockIdx.x >> 3) / (a.B * a.Hkv) * 8 + (int)(blockIdx.x & 7);
+    g = (int)(blockIdx.x >> 3) % a.Hkv;
+    b = (int)(blockIdx.x >> 3) / a.Hkv % a.B;
+    if (c >= a.n_chunks) return;
+  } else {
+    const int lid = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    if (lid >= a.n_units) return;
+    c = lid % a.n_chunks;
+    g = lid / a.n_chunks;
+    b = 0;
+  }
   int Pb = a.prefix_len[b];
   Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
   const int L = Pb + a.N;
@@ -1049,23 +1059,28 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   float* qs = reinterpret_cast<float*>(smem + RG::MAIN + RG::PT_CAP * 4);
   T* qbt = reinterpret_cast<T*>(smem + RG::MAIN + RG::PT_CAP * 4 + RG::AUX_FLOATS * 4);
 
-  // ---- workgroup -> (sequence, KV head, chunk, row block); neighbours share an XCD
-  const int per = gridDim.x >> 3;
-  const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lid >= a.n_units) return;
-  const int rb = lid % a.RB;
-  int rest = lid / a.RB;
-  const int c = rest % a.n_chunks;
-  rest /= a.n_chunks;
-  const int g = rest % a.Hkv;
-  const int b = rest / a.Hkv;
+  // ---- workgroup -> (sequence, KV head, chunk, row block).  Chunk c runs on
+  // XCD c % 8 (blockIdx % 8 picks the XCD), so every XCD gets a slice of every
+  // sequence and head, whatever the sequence lengths; the row blocks of a chunk,
+  // which read the same K/V, share that XCD's L2.
+  int wk = (int)(blockIdx.x >> 3);
+  const int rb = wk % a.RB;
+  wk /= a.RB;
+  const int g = wk % a.Hkv;
+  wk /= a.Hkv;
+  const int b = wk % a.B;
+  const int c = wk / a.B * 8 + (int)(blockIdx.x & 7);
+  if (c >= a.n_chunks) return;
   int Pb = a.prefix_len[b];
   Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
   const int L = Pb + a.N;
-  const int nst_seq = (L + RG::SK - 1) / RG::SK;  // balanced split of whole stages
-  const int c0 = (int)((long long)c * nst_seq / a.n_chunks) * RG::SK;
-  const int c1 = min((int)((long long)(c + 1) * nst_seq / a.n_chunks) * RG::SK, L);
-  const int n_st = c1 > c0 ? (c1 - c0 + RG::SK - 1) / RG::SK : 0;
+  // fixed-length chunks (a whole number of stages): a sequence shorter than the
+  // longest has fewer chunks, and its chunks past the end do nothing (the merge
+  // reads only chunks below P_b + N), so workgroups are of similar length
+  const int c0 = c * a.chunk;
+  if (c0 >= L) return;
+  const int c1 = min(c0 + a.chunk, L);
+  const int n_st = (c1 - c0 + RG::SK - 1) / RG::SK;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1552,7 +1567,8 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
     if (want < 1) want = 1;
     p.n_chunks = (int)want;
     p.chunk = (int)(((nbk + want - 1) / want + 1) * 32);  // longest chunk, in keys
-    p.n_wg = (int)((units * p.n_chunks + 7) / 8 * 8);
+    // batches put chunk c on XCD c % 8; one sequence keeps whole heads on an XCD
+    p.n_wg = B > 1 ? (int)(units * 8 * ((p.n_chunks + 7) / 8)) : (int)((units * p.n_chunks + 7) / 8 * 8);
   }
   const int rtiles = (p.R + 31) / 32;
   if (p.treek) {
@@ -1583,7 +1599,9 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
     // wave of workgroups over the 256 CUs (occ per CU)
     const long long nst = (Lmax + SK - 1) / SK;
     long long nc = (256LL * occ + units / 2) / units;
-    const long long max_st = 4096 / SK;  // chunks of at most 4096 keys: mixed-length batches stay balanced
+    // chunks of at most 4096 keys (2048 for the tree kernel, whose chunks have a fixed
+    // length): the longest workgroups bound the tail of mixed-length batches
+    const long long max_st = (p.treek ? 2048 : 4096) / SK;
     if (nc < (nst + max_st - 1) / max_st) nc = (nst + max_st - 1) / max_st;
     if (nc > nst) nc = nst;
     if (nc < 1) nc = 1;
@@ -1595,7 +1613,8 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
     if (nc > kMaxChunks) nc = kMaxChunks;
     p.n_chunks = (int)nc;
     p.chunk = (int)(((nst + nc - 1) / nc) * SK);  // longest chunk, in keys
-    p.n_wg = (int)((units * p.n_chunks + 7) / 8 * 8);
+    // the tree kernel puts chunk c on XCD c % 8; verify_main keeps neighbouring chunks together
+    p.n_wg = p.treek ? (int)(units * 8 * ((p.n_chunks + 7) / 8)) : (int)((units * p.n_chunks + 7) / 8 * 8);
   }
   size_t off = 0;
   p.off_o = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * D * 4);
@@ -1696,7 +1715,7 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
   a.P_max = p.P_max; a.chunk = p.chunk; a.n_chunks = p.n_chunks;
   a.s_stride = p.P_max + 32;
   a.n_units = p.B * p.Hkv * p.RB * p.n_chunks;
-  a.all_chunks = 1;  // both main kernels write a partial for every chunk
+  a.all_chunks = p.treek ? 0 : 1;  // the tree kernel writes partials only for chunks below P_b + N
   a.ps_shift = -1;
   if (kv.page_table && kv.page_size > 0 && (kv.page_size & (kv.page_size - 1)) == 0) {
     a.ps_shift = 0;
