@@ -599,7 +599,8 @@ struct WaveRing {
   static constexpr int NSW = D == 128 ? 2 : 4;   // blocks in a wave's ring
   static constexpr int WAVE = NSW * BLK;
   static constexpr int RING = 4 * WAVE;
-  static constexpr int EPI = 4 * 32 * (D + 1) * 4 + 4 * 32 * 2 * 4;
+  static constexpr int EPI_OS = D + 4;          // epilogue row stride (floats): 16-byte pad spreads banks
+  static constexpr int EPI = 4 * 32 * EPI_OS * 4 + 4 * 32 * 4 * 4;
   static constexpr int MAIN = RING > EPI ? RING : EPI;
   static constexpr int PT_CAP = 1024;            // cached page-table entries per chunk
   static constexpr int AUX_FLOATS = 512;
@@ -992,43 +993,67 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
   }
   flush_scores();
 
-  // ---- epilogue: combine the four waves (same rows, disjoint keys), write (m, l, o) partials
-  wait_vm_lgkm0<0>();
-  __syncthreads();
-  constexpr int OS = D + 1;
-  float* lo_ = reinterpret_cast<float*>(smem);  // [4 waves][32 rows][D+1]
-  float* lml = lo_ + 4 * 32 * OS;                // [4 waves][32 rows][2]
+  // ---- epilogue: combine the four waves (same rows, disjoint keys), write (m, l, o) partials.
+  // No copy is in flight any more (the last block waited for all of them); the
+  // score stores may be, and nothing here needs them, so only LDS is waited for.
+  // Each wave rescales its own accumulators to the rows' common maximum, the
+  // rescaled tiles meet in LDS, and all threads sum them in wave order.
+  wait_lgkm0();
+  barrier_only();
+  constexpr int OS = WRg::EPI_OS;
+  float* lo_ = reinterpret_cast<float*>(smem);  // [4 waves][32 rows][OS]
+  float* lml = lo_ + 4 * 32 * OS;                // [4 waves][32 rows][m, l, -, -]
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float lt = half_sum(l[rt]);
-    if (rt > 0) __syncthreads();
+    if (rt > 0) {  // the previous tile's reads are done before its LDS is reused
+      wait_lgkm0();
+      barrier_only();
+    }
+    if (h == 0) lml[(wave * 32 + lane32) * 4] = m[rt];
+    wait_lgkm0();
+    barrier_only();
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, lml[(w * 32 + lane32) * 4]);
+    const float wt = (M == kNegInf || m[rt] == kNegInf) ? 0.f : fast_exp2(m[rt] - M);
+    float* orow = lo_ + (wave * 32 + lane32) * OS;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) lo_[(wave * 32 + lane32) * OS + 32 * db + kappa(v, h)] = o[rt][db][v];
-    if (h == 0) {
-      lml[(wave * 32 + lane32) * 2 + 0] = m[rt];
-      lml[(wave * 32 + lane32) * 2 + 1] = lt;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < 32 * D; idx += 256) {
-      const int d = idx % D, r = idx / D;
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd + 4 * h) =
+            f32x4{wt * o[rt][db][4 * qd], wt * o[rt][db][4 * qd + 1], wt * o[rt][db][4 * qd + 2], wt * o[rt][db][4 * qd + 3]};
+    if (h == 0) lml[(wave * 32 + lane32) * 4 + 1] = wt * lt;
+    wait_lgkm0();
+    barrier_only();
+    // thread -> (row, 16 columns): four float4 groups, each summed over the waves in order
+    {
+      constexpr int TPR = 256 / 32;      // threads per row
+      constexpr int CPT = D / TPR;       // columns per thread
+      const int r = tid / TPR, cg = tid % TPR;
       const int row = rt * 32 + r;
-      if (row >= a.R) continue;
-      float M = kNegInf;
+      f32x4 acc[CPT / 4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, lml[(w * 32 + r) * 2]);
-      float acc = 0.f, lsum = 0.f;
+      for (int i = 0; i < CPT / 4; ++i) {
+        const int d = cg * CPT + 4 * i;
+        acc[i] = *reinterpret_cast<const f32x4*>(lo_ + (0 * 32 + r) * OS + d);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = lml[(w * 32 + r) * 2];
-        const float wt = (M == kNegInf) ? 0.f : fast_exp2(mw - M);
-        acc += wt * lo_[(w * 32 + r) * OS + d];
-        lsum += wt * lml[(w * 32 + r) * 2 + 1];
+        for (int w = 1; w < 4; ++w) acc[i] += *reinterpret_cast<const f32x4*>(lo_ + (w * 32 + r) * OS + d);
       }
-      const long long rec = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks + c;
-      a.ws_o[rec * D + d] = acc;
-      if (d == 0) a.ws_ml[rec] = f32x2{M, lsum};
+      if (row < a.R) {
+        const long long rec = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks + c;
+#pragma unroll
+        for (int i = 0; i < CPT / 4; ++i) *reinterpret_cast<f32x4*>(a.ws_o + rec * D + cg * CPT + 4 * i) = acc[i];
+        if (cg == 0) {
+          float Mr = kNegInf, Lr = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, lml[(w * 32 + r) * 4]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) Lr += lml[(w * 32 + r) * 4 + 1];
+          a.ws_ml[rec] = f32x2{Mr, Lr};
+        }
+      }
     }
   }
 }
