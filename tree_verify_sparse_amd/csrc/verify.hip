@@ -1179,6 +1179,14 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
       qf[ks] = row_ok ? x : bf16x8{};
     }
   }
+  // ancestor bitset of this lane's node (tree, chunk reaching the verify
+  // tokens): loaded now, so its latency overlaps the score-operand setup below
+  uint32_t anc[kAncWords] = {};
+  const bool need_anc = a.tree && c1 > Pb;
+  if (need_anc) {
+#pragma unroll
+    for (int w = 0; w < kAncWords; ++w) anc[w] = a.ws_anc[((long long)b * a.N + t_node) * kAncWords + w];
+  }
 
   // ---- score operand: scale * qbar_g split into bf16 hi + mid + lo (B columns 0..2)
   const bool wg_scores = a.do_scores && c0 < Pb;
@@ -1223,14 +1231,9 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
     __syncthreads();
   }
 
-  // ---- ancestor bitset of this lane's node (tree, chunk reaching the verify tokens)
-  uint32_t anc[kAncWords] = {};
-  if (a.tree && c1 > Pb) {
+  if (need_anc) {
 #pragma unroll
-    for (int w = 0; w < kAncWords; ++w) {
-      anc[w] = a.ws_anc[((long long)b * a.N + t_node) * kAncWords + w];
-      asm volatile("" ::"v"(anc[w]));  // wait for the load here, not inside the loop
-    }
+    for (int w = 0; w < kAncWords; ++w) asm volatile("" ::"v"(anc[w]));  // wait for the loads here, not inside the loop
   }
 
   // ---- per-lane LDS offsets of the operand reads inside a 32-key block
@@ -1366,8 +1369,8 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   for (int i = 0; i < n_plain; ++i) stage(i, std::false_type{});
   for (int i = n_plain; i < n_st; ++i) stage(i, std::true_type{});
 
-  // ---- epilogue: this wave's rows are its own -> (m, l, o) partials straight to the workspace
-  wait_vm_lgkm0<0>();
+  // ---- epilogue: this wave's rows are its own -> (m, l, o) partials straight to
+  // the workspace (no copy is in flight; the score stores need no wait)
   const float lt = half_sum(l);
   if (row_ok) {
     const long long rec = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks + c;
