@@ -27,6 +27,8 @@ from .reference import (  # noqa: F401
     verify_scores_grouped,
     topk_select,
     sparse_draft_attention,
+    compact_kv,
+    dense_draft_attention,
     run_step,
     bf16_bits_to_f64,
 )

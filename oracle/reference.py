@@ -32,6 +32,10 @@ Pins (tests/test_oracle_*.py):
                           argmax) on tiny inputs with exact ties; golden cases
   sparse_draft_attention -- idx = whole prefix == dense decode; permutation
                           invariance; golden 2-key case
+  compact_kv, dense_draft_attention -- compacted rows == sparse_draft_attention
+                          over the same list; a tail == the tail rows placed in
+                          a cache past the prefix and listed; one row == its V
+                          row exactly; row-permutation invariance
 """
 from __future__ import annotations
 
@@ -258,6 +262,53 @@ def sparse_draft_attention(q1: np.ndarray, dtype: str, kv: KVCache,
             hs = list(range(g * G, (g + 1) * G))
             lg = scale * (Kg @ qf[b, hs].T)                        # [n][G]
             out[b, hs] = _softmax_attend(lg, Vg)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# draft loop over a compacted KV: the draft model's attention runs once per
+# draft token over the same selected set (Vegas §2 step 3; §3, where the sparse
+# kernel is called several times per step), so the selected rows are gathered
+# once into a dense buffer, and each draft token's own K/V row is appended
+# behind them (its tail) before its decode attends to all rows so far
+
+def compact_kv(kv: KVCache, idx: Sequence[np.ndarray], cap: int) -> tuple[np.ndarray, np.ndarray]:
+    """Dense K and V buffers [B][cap][Hkv][D] in the cache's storage type: row j
+    of sequence b is the row of logical position idx[b][j] (all KV heads);
+    rows from len(idx[b]) on are zero."""
+    B = len(idx)
+    Hkv, D = kv.k.shape[1], kv.k.shape[2]
+    ck = np.zeros((B, cap, Hkv, D), dtype=kv.k.dtype)
+    cv = np.zeros((B, cap, Hkv, D), dtype=kv.v.dtype)
+    for b in range(B):
+        ib = np.asarray(idx[b], dtype=np.int64)[:cap]
+        if ib.size:
+            sl = kv.slots(b, ib)
+            ck[b, : ib.size] = kv.k[sl]
+            cv[b, : ib.size] = kv.v[sl]
+    return ck, cv
+
+
+def dense_draft_attention(q1: np.ndarray, dtype: str, ck: np.ndarray, cv: np.ndarray,
+                          n_rows: Sequence[int], scale: float, Hkv: int) -> np.ndarray:
+    """One query per sequence attending to rows [0, n_rows[b]) of dense K/V
+    buffers [B][cap][Hkv][D] (the compacted set and the draft tail).
+
+    q1: [B][Hq][D] storage.  Returns float64 [B][Hq][D]; n_rows[b] = 0 gives 0.
+    """
+    qf = _f64(q1, dtype)
+    B, Hq, D = qf.shape
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = int(n_rows[b])
+        if n <= 0:
+            continue
+        for g in range(Hkv):
+            Kg = _f64(ck[b, :n, g], dtype)
+            Vg = _f64(cv[b, :n, g], dtype)
+            hs = list(range(g * G, (g + 1) * G))
+            out[b, hs] = _softmax_attend(scale * (Kg @ qf[b, hs].T), Vg)
     return out
 
 

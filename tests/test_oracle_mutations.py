@@ -109,6 +109,24 @@ def test_sparse_drops_last_index_is_caught(monkeypatch):
     assert _fails(pins.test_golden_sparse_two_keys)
 
 
+def test_dense_draft_drops_last_row_is_caught(monkeypatch):
+    orig = ref.dense_draft_attention
+
+    def drop_last(q1, dtype, ck, cv, n_rows, scale, Hkv):
+        return orig(q1, dtype, ck, cv, [max(0, int(n) - 1) for n in n_rows], scale, Hkv)
+    _patch(monkeypatch, "dense_draft_attention", drop_last)
+    assert _fails(pins.test_compacted_draft_equals_sparse_list, "bf16", "contiguous")
+
+
+def test_compact_shifted_rows_is_caught(monkeypatch):
+    orig = ref.compact_kv
+
+    def shifted(kv, idx, cap):  # gathers the position after each listed one
+        return orig(kv, [np.asarray(i) + 1 for i in idx], cap)
+    _patch(monkeypatch, "compact_kv", shifted)
+    assert _fails(pins.test_compacted_draft_equals_sparse_list, "bf16", "contiguous")
+
+
 def test_unmutated_oracle_passes_the_same_checks():
     # the same check functions pass on the real oracle (guards against vacuous mutation tests)
     pins.test_golden_attention_three_keys()
@@ -116,3 +134,4 @@ def test_unmutated_oracle_passes_the_same_checks():
     pins.test_golden_scores_small()
     pins.test_golden_topk_ties()
     pins.test_golden_sparse_two_keys()
+    pins.test_compacted_draft_equals_sparse_list("bf16", "contiguous")

@@ -334,3 +334,73 @@ def test_topk_signed_zero_and_wide():
     got = oracle.topk_select(s, 300, 17)
     thr = np.sort(s)[::-1][16]
     assert (s[got] >= thr).all() and len(got) == 17
+
+
+# ----------------------------------------------------------------------------- compacted draft loop
+
+def _tail_cache(wl, tail_k, tail_v, steps):
+    """Copy of the cache with tail row t of sequence b at logical position P_b + N + t."""
+    k2, v2 = wl.k.copy(), wl.v.copy()
+    kv = KVCache.of(wl)
+    for b in range(wl.B):
+        sl = kv.slots(b, int(wl.P[b]) + wl.N + np.arange(steps))
+        k2[sl] = tail_k[:steps, b]
+        v2[sl] = tail_v[:steps, b]
+    return KVCache(k2, v2, wl.dtype, wl.layout, wl.seq_stride, wl.page_size, wl.page_table)
+
+
+@pytest.mark.parametrize("dtype,layout", [("bf16", "contiguous"), ("f32", "paged")])
+def test_compacted_draft_equals_sparse_list(dtype, layout):
+    """Rows gathered once and attended densely == the sparse step over the same
+    list (the pinned sparse_draft_attention), with and without a tail."""
+    from workloads import make_tail_rows
+    wl = make_custom(seed=21, dtype=dtype, B=2, Hq=8, Hkv=2, D=64, P=[150, 90], N=3, q_std_mult=4.0,
+                     layout=layout, page_size=16, seq_extra=8)
+    kv = KVCache.of(wl)
+    rng = np.random.default_rng(3)
+    idx = [np.sort(rng.choice(int(wl.P[b]), n, replace=False)) for b, n in enumerate((40, 17))]
+    n = [len(x) for x in idx]
+    cap = 48
+    ck, cv = oracle.compact_kv(kv, idx, cap)
+    assert (ck[1, 17:] == 0).all() and (cv[0, 40:] == 0).all()
+    a = oracle.dense_draft_attention(wl.dq[0], dtype, ck, cv, n, wl.scale, 2)
+    b = oracle.sparse_draft_attention(wl.dq[0], dtype, kv, idx, wl.scale, 2)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    # a tail of s drafted tokens behind the set == those rows past the prefix, listed
+    tail_k, tail_v = make_tail_rows(5, 4, wl.B, 2, 64, dtype)
+    for s in (1, 2, 4):
+        ck2, cv2 = ck.copy(), cv.copy()
+        for bb in range(wl.B):
+            ck2[bb, n[bb]: n[bb] + s] = tail_k[:s, bb]
+            cv2[bb, n[bb]: n[bb] + s] = tail_v[:s, bb]
+        dense = oracle.dense_draft_attention(wl.dq[0], dtype, ck2, cv2, [x + s for x in n], wl.scale, 2)
+        kv2 = _tail_cache(wl, tail_k, tail_v, s)
+        idx2 = [np.concatenate([idx[bb], int(wl.P[bb]) + wl.N + np.arange(s)]) for bb in range(wl.B)]
+        sparse = oracle.sparse_draft_attention(wl.dq[0], dtype, kv2, idx2, wl.scale, 2)
+        np.testing.assert_allclose(dense, sparse, rtol=1e-12, atol=1e-15)
+
+
+def test_dense_draft_single_row_permutation_and_empty():
+    wl = make_custom(seed=22, dtype="bf16", B=2, Hq=8, Hkv=2, D=128, P=120, N=2, q_std_mult=4.0)
+    kv = KVCache.of(wl)
+    idx = [np.arange(0, 120, 3), np.arange(5, 60)]
+    ck, cv = oracle.compact_kv(kv, idx, 64)
+    # one row: softmax over a single logit is 1, so the output is that row's V exactly
+    one = oracle.dense_draft_attention(wl.dq[0], "bf16", ck, cv, [1, 1], wl.scale, 2)
+    for b in range(2):
+        for h in range(8):
+            assert np.array_equal(one[b, h], oracle.bf16_bits_to_f64(cv[b, 0, h // 4]))
+    # rows in another order give the same output
+    n = [40, 55]
+    base = oracle.dense_draft_attention(wl.dq[0], "bf16", ck, cv, n, wl.scale, 2)
+    rng = np.random.default_rng(1)
+    ckp, cvp = ck.copy(), cv.copy()
+    for b in range(2):
+        perm = rng.permutation(n[b])
+        ckp[b, : n[b]] = ck[b, perm]
+        cvp[b, : n[b]] = cv[b, perm]
+    np.testing.assert_allclose(oracle.dense_draft_attention(wl.dq[0], "bf16", ckp, cvp, n, wl.scale, 2), base,
+                               rtol=1e-12, atol=1e-15)
+    # no rows: zero output
+    z = oracle.dense_draft_attention(wl.dq[0], "bf16", ck, cv, [0, 0], wl.scale, 2)
+    assert (z == 0).all()

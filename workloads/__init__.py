@@ -22,6 +22,7 @@ from .gen import (  # noqa: F401
     make_workload,
     make_custom,
     make_score_vector,
+    make_tail_rows,
     CONFIG_NAMES,
     bf16_bits_from_f32,
     f32_from_bf16_bits,

@@ -33,7 +33,7 @@ import numpy as np
 from .tree import best_first_tree, chain_parents, depth_logprobs
 
 # generator stream ids (one stream per tensor)
-_S_Q, _S_K, _S_V, _S_HEAVY, _S_TREE, _S_DQ, _S_LEN, _S_PAGES, _S_SCORES = range(9)
+_S_Q, _S_K, _S_V, _S_HEAVY, _S_TREE, _S_DQ, _S_LEN, _S_PAGES, _S_SCORES, _S_TAIL = range(10)
 
 CONFIG_NAMES = {
     1: "tiny-fp32-chain-p512",
@@ -310,6 +310,16 @@ def make_workload(cfg: int, seed: int = 0) -> Workload:
                            tree="best_first", tree_depth=6, score_rows="all", k_sel="5pct",
                            decode_steps=1, layout="paged", page_size=16, name=name)
     raise ValueError(cfg)
+
+
+def make_tail_rows(seed, steps: int, B: int, Hkv: int, D: int, dtype: str) -> tuple[np.ndarray, np.ndarray]:
+    """K and V rows of `steps` drafted tokens per sequence (their tail behind a
+    compacted set), storage type, shape [steps][B][Hkv][D], N(0, 1/D) like the cache."""
+    r = np.random.default_rng([int(x) for x in np.atleast_1d(seed)] + [_S_TAIL])
+    sd = 1.0 / np.sqrt(D)
+    k = _draw(r, (steps, B, Hkv, D), sd)
+    v = _draw(r, (steps, B, Hkv, D), sd)
+    return _store(k, dtype), _store(v, dtype)
 
 
 def make_score_vector(seed: int, n: int, kind: str = "normal") -> np.ndarray:
