@@ -13,6 +13,9 @@
  *   sv_topk_select        the k highest-scoring prefix entries of each sequence.
  *   sv_sparse_draft_attn  the next draft step's decode attention restricted to
  *                         a gathered index set.
+ *   sv_compact_kv, sv_dense_draft_attn   the same draft steps over the set
+ *                         gathered once into dense buffers, plus a tail of
+ *                         drafted tokens' rows.
  *
  * Sources (technical-summary pages on gist.science/pt/paper/...):
  *   Vegas (2602.07223): §2 "Mecanismo Central" steps 1-3 (verify with full
@@ -171,6 +174,44 @@ sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int
                                const sv_kv_cache* kv, const int32_t* idx, int idx_stride,
                                const int32_t* n_idx, int max_idx, float softmax_scale, void* out,
                                void* workspace, size_t workspace_bytes, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Draft loop over a compacted KV.  The draft model's attention is called once
+ * per draft token over the same selected set (Vegas §2 step 3; §3, the sparse
+ * kernel invoked several times per speculative step), so the set is gathered
+ * once into dense buffers and each drafted token's own K/V row is appended
+ * behind it (its tail) before the token's decode reads all rows so far.
+ *
+ * sv_compact_kv: for j < n_b = min(n_idx[b], max_idx, cap), copy the K and V
+ * rows (all Hkv heads) of logical position idx[b][j] into row j of sequence b:
+ *   ck, cv       device [B][cap][Hkv][D] dtype, 16-byte aligned, caller-owned;
+ *                rows j >= n_b are left untouched (the caller appends tail
+ *                rows there with plain copies).
+ *   kv, idx, idx_stride, n_idx, max_idx   as for sv_sparse_draft_attn.
+ * Bytes are copied unchanged (results are bit-identical to the cache rows).
+ */
+sv_status sv_compact_kv(sv_dtype dtype, int B, int Hkv, int D, const sv_kv_cache* kv,
+                        const int32_t* idx, int idx_stride, const int32_t* n_idx, int max_idx,
+                        void* ck, void* cv, int cap, sv_stream stream);
+
+/* sv_dense_draft_attn: decode attention of one query per sequence over rows
+ * [0, n_rows[b]) of dense buffers (the compacted set, then the tail, the last
+ * row being the drafted token's own).
+ *   q            [B][Hq][D] dtype.
+ *   ck, cv       device [B][cap][Hkv][D] dtype.
+ *   n_rows       device int32[B], 0 <= n_rows[b] <= cap (larger values are
+ *                clamped to cap); 0 gives a zero output.
+ *   out          [B][Hq][D] dtype (round-to-nearest-even from fp32).
+ *   workspace    sv_dense_draft_workspace_size(B, Hq, Hkv, D, cap, dtype) bytes;
+ *                contents on entry are ignored.
+ * Same result (up to rounding order) as sv_sparse_draft_attn over the listed
+ * positions of the rows.
+ */
+size_t sv_dense_draft_workspace_size(int B, int Hq, int Hkv, int D, int cap, sv_dtype dtype);
+sv_status sv_dense_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D,
+                              const void* ck, const void* cv, int cap, const int32_t* n_rows,
+                              float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                              sv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* Optional timing hook for profiling: while set (non-NULL), every

@@ -121,6 +121,38 @@ def test_topk_and_sparse_reject_bad_arguments():
     assert "workspace" in lib.sv_last_error().decode()
 
 
+def test_compact_and_dense_draft_reject_bad_arguments():
+    lib = _lib.load()
+    kv = _kv()
+    cp = lib.sv_compact_kv
+    args = lambda **k: dict(dict(dt=_lib.SV_BF16, B=1, Hkv=8, D=128, idx=FAKE, stride=10, n=FAKE, max_idx=10,  # noqa: E731
+                                 ck=FAKE, cv=FAKE, cap=16), **k)
+
+    def compact(**k):
+        a = args(**k)
+        return cp(a["dt"], a["B"], a["Hkv"], a["D"], ctypes.byref(kv), a["idx"], a["stride"], a["n"], a["max_idx"],
+                  a["ck"], a["cv"], a["cap"], None)
+    assert compact(max_idx=11) == _lib.SV_E_INVALID                 # max_idx > idx_stride
+    assert compact(cap=0) == _lib.SV_E_INVALID
+    assert compact(D=96) == _lib.SV_E_UNSUPPORTED
+    assert compact(dt=3) == _lib.SV_E_UNSUPPORTED
+    assert compact(ck=FAKE + 8) == _lib.SV_E_INVALID
+    assert "aligned" in lib.sv_last_error().decode()
+    assert compact(n=None) == _lib.SV_E_INVALID
+    assert compact(B=0, ck=None, cv=None) == _lib.SV_OK
+    dd = lib.sv_dense_draft_attn
+    need = lib.sv_dense_draft_workspace_size(1, 32, 8, 128, 4096, _lib.SV_BF16)
+    # the decode is one verify query over a contiguous buffer of cap slots per sequence
+    assert need == lib.sv_verify_workspace_size(1, 1, 32, 8, 128, 4095, _lib.SV_BF16, 0, 0, 0) > 0
+    assert lib.sv_dense_draft_workspace_size(1, 32, 8, 128, 0, _lib.SV_BF16) == 0
+    assert dd(FAKE, _lib.SV_BF16, 1, 32, 8, 128, FAKE, FAKE, 0, FAKE, 0.0, FAKE, FAKE, need, None) == _lib.SV_E_INVALID
+    assert dd(FAKE, _lib.SV_BF16, 1, 30, 8, 128, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, FAKE, need, None) == _lib.SV_E_INVALID
+    assert dd(FAKE, _lib.SV_BF16, 1, 32, 8, 128, FAKE, FAKE, 4096, None, 0.0, FAKE, FAKE, need, None) == _lib.SV_E_INVALID
+    assert dd(FAKE, _lib.SV_BF16, 1, 32, 8, 128, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, FAKE, need - 1,
+              None) == _lib.SV_E_WORKSPACE
+    assert dd(None, _lib.SV_BF16, 0, 32, 8, 128, None, None, 4096, None, 0.0, None, None, 0, None) == _lib.SV_OK
+
+
 def test_timing_events_must_pair():
     lib = _lib.load()
     assert lib.sv_set_verify_timing_events(FAKE, None) == _lib.SV_E_INVALID

@@ -8,6 +8,8 @@ requires the built library and a gfx950 device, and there is no fallback.
     out, scores = verify_attn(q, kv, prefix_len, parent=None, score_rows=[0, N-1])
     idx, count  = topk_select(scores, prefix_len, k, k_max)
     draft_out   = sparse_draft_attn(q1, kv, idx, count)
+    ck, cv      = compact_kv(kv, idx, count, cap)          # once per selection
+    draft_out   = dense_draft_attn(q1, ck, cv, n_rows)     # per draft token
 """
 from __future__ import annotations
 
@@ -21,9 +23,9 @@ import torch
 from . import _lib
 from ._lib import SvError, SV_F32, SV_BF16  # noqa: F401
 
-__all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn",
-           "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size", "timing_events", "SvError",
-           "lib"]
+__all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn", "compact_kv",
+           "dense_draft_attn", "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size",
+           "dense_draft_workspace_size", "timing_events", "SvError", "lib"]
 
 
 def lib() -> ctypes.CDLL:
@@ -182,6 +184,49 @@ def sparse_draft_attn(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, n_idx: to
     _lib.check(L.sv_sparse_draft_attn(_ptr(q), dt, B, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(idx), stride,
                                       _ptr(n_idx), max_idx, float(scale), _ptr(out), wptr, wlen,
                                       _stream(q.device)))
+    return out
+
+
+def compact_kv(kv: KVCache, idx: torch.Tensor, n_idx: torch.Tensor, cap: int, *, max_idx: Optional[int] = None,
+               ck: Optional[torch.Tensor] = None, cv: Optional[torch.Tensor] = None):
+    """sv_compact_kv: the listed rows gathered into dense ck, cv [B][cap][Hkv][D]
+    (rows past n_idx[b] are left as they were; new buffers start zeroed)."""
+    L = lib()
+    B = int(idx.shape[0])
+    stride = int(idx.shape[1])
+    max_idx = stride if max_idx is None else int(max_idx)
+    shape = (B, cap, kv.Hkv, kv.D)
+    if ck is None:
+        ck = torch.zeros(shape, dtype=kv.k.dtype, device=kv.k.device)
+    if cv is None:
+        cv = torch.zeros(shape, dtype=kv.v.dtype, device=kv.v.device)
+    if tuple(ck.shape) != shape or tuple(cv.shape) != shape:
+        raise ValueError(f"ck and cv must be {shape}")
+    kvs = kv.c_struct()
+    _lib.check(L.sv_compact_kv(_dtype_code(kv.k), B, kv.Hkv, kv.D, ctypes.byref(kvs), _ptr(idx), stride,
+                               _ptr(n_idx), max_idx, _ptr(ck), _ptr(cv), int(cap), _stream(kv.k.device)))
+    return ck, cv
+
+
+def dense_draft_workspace_size(B, Hq, Hkv, D, cap, dtype) -> int:
+    return int(lib().sv_dense_draft_workspace_size(B, Hq, Hkv, D, cap, dtype))
+
+
+def dense_draft_attn(q: torch.Tensor, ck: torch.Tensor, cv: torch.Tensor, n_rows: torch.Tensor, *,
+                     scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[Workspace] = None):
+    """sv_dense_draft_attn: q [B][Hq][D] over rows [0, n_rows[b]) of ck, cv [B][cap][Hkv][D]."""
+    L = lib()
+    B, Hq, D = (int(x) for x in q.shape)
+    if ck.dim() != 4 or ck.shape != cv.shape or int(ck.shape[0]) != B or int(ck.shape[3]) != D:
+        raise ValueError("ck and cv must both be [B][cap][Hkv][D]")
+    cap, Hkv = int(ck.shape[1]), int(ck.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _dtype_code(q)
+    wptr, wlen = _ws(workspace, "dense").get(dense_draft_workspace_size(B, Hq, Hkv, D, cap, dt), q.device)
+    _lib.check(L.sv_dense_draft_attn(_ptr(q), dt, B, Hq, Hkv, D, _ptr(ck), _ptr(cv), cap, _ptr(n_rows),
+                                     float(scale), _ptr(out), wptr, wlen, _stream(q.device)))
     return out
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -174,6 +175,54 @@ sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int
   return hip_status(sv::launch_sparse(p, (int)dtype, q, kv_args(kv), idx, idx_stride, n_idx,
                                       resolve_scale(softmax_scale, D), out, workspace, stream),
                     "sv_sparse_draft_attn launch");
+}
+
+sv_status sv_compact_kv(sv_dtype dtype, int B, int Hkv, int D, const sv_kv_cache* kv, const int32_t* idx,
+                        int idx_stride, const int32_t* n_idx, int max_idx, void* ck, void* cv, int cap,
+                        sv_stream stream) {
+  sv_status st;
+  if ((st = check_dtype(dtype))) return st;
+  if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
+  if ((st = check_heads(Hkv, Hkv, D))) return st;
+  if (max_idx < 0 || idx_stride < max_idx) return fail(SV_E_INVALID, "need 0 <= max_idx <= idx_stride");
+  if (cap < 1) return fail(SV_E_INVALID, "cap must be >= 1");
+  if (B == 0) return ok();
+  if (!n_idx || !ck || !cv || (!idx && max_idx > 0)) return fail(SV_E_INVALID, "idx, n_idx, ck and cv must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(ck) | reinterpret_cast<uintptr_t>(cv)) & 15)
+    return fail(SV_E_INVALID, "ck and cv must be 16-byte aligned");
+  if ((st = check_kv(kv, B))) return st;
+  return hip_status(sv::launch_compact((int)dtype, B, Hkv, D, kv_args(kv), idx, idx_stride, n_idx, max_idx, ck, cv,
+                                       cap, stream),
+                    "sv_compact_kv launch");
+}
+
+size_t sv_dense_draft_workspace_size(int B, int Hq, int Hkv, int D, int cap, sv_dtype dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (D != 64 && D != 128) || cap < 1 ||
+      (dtype != SV_F32 && dtype != SV_BF16))
+    return 0;
+  return sv::plan_verify(B, 1, Hq, Hkv, D, cap - 1, (int)dtype, false, 0, 0).bytes;
+}
+
+sv_status sv_dense_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D, const void* ck,
+                              const void* cv, int cap, const int32_t* n_rows, float softmax_scale, void* out,
+                              void* workspace, size_t workspace_bytes, sv_stream stream) {
+  sv_status st;
+  if ((st = check_dtype(dtype))) return st;
+  if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
+  if ((st = check_heads(Hq, Hkv, D))) return st;
+  if (cap < 1) return fail(SV_E_INVALID, "cap must be >= 1");
+  if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return fail(SV_E_INVALID, "softmax_scale must be finite and >= 0");
+  if (B == 0) return ok();
+  if (!q || !out || !ck || !cv || !n_rows) return fail(SV_E_INVALID, "q, out, ck, cv and n_rows must be non-NULL");
+  // the dense buffers are a contiguous cache with cap slots per sequence; the
+  // decode is verification of N = 1 query whose prefix is its first n - 1 rows
+  const sv::VerifyPlan p = sv::plan_verify(B, 1, Hq, Hkv, D, cap - 1, (int)dtype, false, 0, 0);
+  if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
+    return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
+  const sv::KvArgs kv{ck, cv, nullptr, 1, 0, (long long)cap, (long long)B * cap};
+  const int e = sv::launch_verify(p, q, kv, n_rows, nullptr, nullptr, 0, resolve_scale(softmax_scale, D), out,
+                                  nullptr, workspace, stream, nullptr, nullptr, -1);
+  return hip_status(e, "sv_dense_draft_attn launch");
 }
 
 }  // extern "C"

@@ -174,6 +174,81 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   }
 }
 
+// Compaction of a selected set: the K and V rows (all KV heads, Hkv * D
+// elements each) of the listed logical positions are copied into dense
+// per-sequence buffers, so that the draft steps that follow read one
+// contiguous stream instead of gathering the set again each time.  One
+// workgroup copies kCompactRows rows of one sequence as 16-byte pieces, every
+// load of a batch issued before any store.
+constexpr int kCompactRows = 16;
+
+struct CompactArgs {
+  KvView kv;
+  const int32_t* idx;
+  const int32_t* n_idx;
+  char* ck;
+  char* cv;
+  int idx_stride, max_idx, cap;
+  int row_pieces;  // 16-byte pieces per row: Hkv * D * sizeof(T) / 16
+};
+
+__global__ void __launch_bounds__(256) compact_rows(const CompactArgs a) {
+  constexpr int U = 4;  // pieces per thread per batch (of K and of V)
+  const int b = blockIdx.y, tid = threadIdx.x;
+  int n = a.n_idx[b];
+  n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
+  n = n > a.cap ? a.cap : n;
+  const int j0 = blockIdx.x * kCompactRows;
+  if (j0 >= n) return;
+  const int nr = min(kCompactRows, n - j0);
+  const int total = nr * a.row_pieces;
+  const long long row_bytes = (long long)a.row_pieces * 16;
+  const char* kb = reinterpret_cast<const char*>(a.kv.k);
+  const char* vb = reinterpret_cast<const char*>(a.kv.v);
+  for (int base = 0; base < total; base += 256 * U) {
+    uint4 kx[U], vx[U];
+    long long dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = base + tid + 256 * u;
+      const int r = e / a.row_pieces, c = e % a.row_pieces;
+      long long sl = -1;
+      if (e < total) sl = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + j0 + r]);
+      if (sl < 0) sl = 0;  // unmapped positions copy slot 0 (a caller-contract violation)
+      dst[u] = e < total ? ((long long)b * a.cap + j0 + r) * row_bytes + c * 16 : -1;
+      kx[u] = *reinterpret_cast<const uint4*>(kb + sl * row_bytes + c * 16);
+      vx[u] = *reinterpret_cast<const uint4*>(vb + sl * row_bytes + c * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (dst[u] >= 0) {
+        *reinterpret_cast<uint4*>(a.ck + dst[u]) = kx[u];
+        *reinterpret_cast<uint4*>(a.cv + dst[u]) = vx[u];
+      }
+    }
+  }
+}
+
+int launch_compact(int dtype, int B, int Hkv, int D, const KvArgs& kv, const int32_t* idx, int idx_stride,
+                   const int32_t* n_idx, int max_idx, void* ck, void* cv, int cap, void* stream) {
+  CompactArgs a{};
+  a.kv = KvView{kv.k, kv.v, kv.page_table, kv.page_size, kv.max_pages, kv.seq_stride, kv.num_slots};
+  a.idx = idx;
+  a.n_idx = n_idx;
+  a.ck = reinterpret_cast<char*>(ck);
+  a.cv = reinterpret_cast<char*>(cv);
+  a.idx_stride = idx_stride;
+  a.max_idx = max_idx;
+  a.cap = cap;
+  a.row_pieces = Hkv * D * (dtype == SV_BF16 ? 2 : 4) / 16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int rows = min(max_idx, cap);
+  if (B == 0 || rows <= 0) return 0;
+  hipLaunchKernelGGL(compact_rows, dim3((rows + kCompactRows - 1) / kCompactRows, B), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
 SparsePlan plan_sparse(int B, int Hq, int Hkv, int D, int max_idx) {
   SparsePlan p{};
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.D = D; p.max_idx = max_idx;

@@ -52,9 +52,15 @@ struct KvArgs {
 };
 
 // Launchers (return a hipError_t as int; 0 = success).
+// len_bias: 0 for verification; -1 turns prefix_len into row counts of a dense
+// decode (N = 1: the query sees rows [0, prefix_len[b]), none when it is 0).
 int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const int32_t* prefix_len,
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
-                  void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop);
+                  void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
+                  int len_bias = 0);
+// Gather the listed rows (all KV heads) into dense [B][cap][Hkv][D] buffers.
+int launch_compact(int dtype, int B, int Hkv, int D, const KvArgs& kv, const int32_t* idx, int idx_stride,
+                   const int32_t* n_idx, int max_idx, void* ck, void* cv, int cap, void* stream);
 int launch_topk(const float* scores, int B, int P_max, const int32_t* prefix_len, const int32_t* k,
                 int k_max, int32_t* idx, int32_t* count, void* ws, void* stream);
 size_t topk_workspace_bytes(int B, int P_max);

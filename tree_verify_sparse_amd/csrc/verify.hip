@@ -94,8 +94,21 @@ struct VerifyArgs {
   int ps_shift;  // log2(page_size) if it is a power of two, else -1
   float scale, scale_log2;
   int n_score_rows;
+  int len_bias;  // 0 for verification; -1 for a decode over rows [0, prefix_len[b]) (see seq_prefix)
   uint16_t score_rows[kMaxNodes];
 };
+
+// P_b of sequence b, clamped to [0, P_max], and in *L the length of its KV
+// range P_b + N.  A decode over the first n rows of a dense buffer passes n
+// with len_bias -1 and N = 1: the query is the last row's token and sees
+// [0, n); n = 0 then means no rows at all (L = 0, a zero output).
+__device__ __forceinline__ int seq_prefix(const VerifyArgs& a, int b, int* L) {
+  int Pb = a.prefix_len[b] + a.len_bias;
+  const bool empty = a.len_bias < 0 && Pb < 0;
+  Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
+  *L = empty ? 0 : Pb + a.N;
+  return Pb;
+}
 
 // key offset (within a 32-key block) of accumulator element v for lane half h
 __device__ __forceinline__ int kappa(int v, int h) { return mfma_row(v, h); }
@@ -151,9 +164,8 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   const int g = rest % a.Hkv;
   const int b = rest / a.Hkv;
 
-  int Pb = a.prefix_len[b];
-  Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
-  const int L = Pb + a.N;
+  int L;
+  const int Pb = seq_prefix(a, b, &L);
   // chunk c covers stages [c * nst / n_chunks, (c + 1) * nst / n_chunks) of
   // this sequence (balanced; an empty chunk still writes an empty partial)
   const int nst_seq = (L + RG::SK - 1) / RG::SK;
@@ -673,9 +685,8 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
     g = lid / a.n_chunks;
     b = 0;
   }
-  int Pb = a.prefix_len[b];
-  Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
-  const int L = Pb + a.N;
+  int L;
+  const int Pb = seq_prefix(a, b, &L);
   const int nbk = (L + 31) >> 5;
 
   const int tid = threadIdx.x;
@@ -1096,9 +1107,8 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   const int b = wk % a.B;
   const int c = wk / a.B * 8 + (int)(blockIdx.x & 7);
   if (c >= a.n_chunks) return;
-  int Pb = a.prefix_len[b];
-  Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
-  const int L = Pb + a.N;
+  int L;
+  const int Pb = seq_prefix(a, b, &L);
   // fixed-length chunks (a whole number of stages): a sequence shorter than the
   // longest has fewer chunks, and its chunks past the end do nothing (the merge
   // reads only chunks below P_b + N), so workgroups are of similar length
@@ -1419,9 +1429,9 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
     const int gr = (int)blockIdx.x * (4 / wpr) + wave / wpr;  // (b, g, row); uniform over a row's waves
     if (gr >= a.B * a.Hkv * a.R) return;
     const int row = gr % a.R, bg = gr / a.R, g = bg % a.Hkv, b = bg / a.Hkv;
-    int Pb = a.prefix_len[b];
-    Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
-    const int nc = a.all_chunks ? a.n_chunks : min((Pb + a.N + a.chunk - 1) / a.chunk, a.n_chunks);
+    int L;
+    seq_prefix(a, b, &L);
+    const int nc = a.all_chunks ? a.n_chunks : min((L + a.chunk - 1) / a.chunk, a.n_chunks);
     const long long rec0 = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks;
     static_assert(D / 4 <= 32, "one float4 column group per lane of a half");
     const int half = lane >> 5, q = lane & 31;
@@ -1725,7 +1735,8 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
 
 int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const int32_t* prefix_len,
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
-                  void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop) {
+                  void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
+                  int len_bias) {
   VerifyArgs a{};
   a.q = q;
   a.out = out;
@@ -1753,6 +1764,7 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.n_score_rows = n_score_rows;
+  a.len_bias = len_bias;
   for (int i = 0; i < n_score_rows && i < kMaxNodes; ++i) a.score_rows[i] = (uint16_t)score_rows[i];
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();

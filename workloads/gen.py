@@ -228,7 +228,7 @@ def make_custom(*, seed, B=1, Hq=4, Hkv=1, D=64, dtype="f32", P=512, N=5,
         page_table = None
     elif layout == "paged":
         seq_stride = 0
-        npages = (L + page_size - 1) // page_size
+        npages = (L + seq_extra + page_size - 1) // page_size  # seq_extra: mapped room past P_b + N
         total = int(npages.sum())
         perm = rng(_S_PAGES).permutation(total).astype(np.int32)
         max_pages = int(npages.max()) if B else 0
