@@ -3,8 +3,11 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 sv_verify_attn (dense tree/chain verification + fused criticality scores) ->
-sv_topk_select -> sv_sparse_draft_attn (one draft query per sequence, or the
-workload's number of draft steps over the same selected set).
+sv_topk_select -> the draft steps (one draft query per sequence, or the
+workload's number of draft steps over the same selected set): each step
+sv_sparse_draft_attn over the selected positions, or (--draft-path compact,
+the default for several draft steps) sv_compact_kv once and then
+sv_dense_draft_attn per step over the gathered rows -- the same attention.
 
 Default workload: the 32k-context Llama-3-8B-shaped layer (B=1, 32 query /
 8 KV heads, D=128, bf16, prefix 32768, chain of 8 verify queries,
@@ -46,6 +49,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kv-copies", type=int, default=0,
                     help="KV copies rotated between steps so that no step hits the 256 MB MALL (0 = auto)")
+    ap.add_argument("--draft-path", choices=["auto", "sparse", "compact"], default="auto",
+                    help="draft steps gather the selected rows each time (sparse), or the set is gathered "
+                         "once into dense buffers and every step streams them (compact); auto: compact "
+                         "when the workload has more than one draft step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
@@ -129,6 +136,22 @@ def main():
               for s in range(n_draft)] for kv in kvs]
     f_verify, f_topk, f_sparse, f_hook = L.sv_verify_attn, L.sv_topk_select, L.sv_sparse_draft_attn, \
         L.sv_set_verify_timing_events
+    # compacted draft loop: the selected rows gathered once per step into dense
+    # [B][k_max][Hkv][D] buffers, every draft step decoding over rows [0, count)
+    draft_path = args.draft_path
+    if draft_path == "auto":
+        draft_path = "compact" if n_draft > 1 else "sparse"
+    if draft_path == "compact" and n_draft > 0:
+        cshape = (wl.B, max(1, kmax), wl.Hkv, wl.D)
+        ck = torch.empty(cshape, dtype=q.dtype, device=dev)
+        cv = torch.empty(cshape, dtype=q.dtype, device=dev)
+        dws_n = L.sv_dense_draft_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, max(1, kmax), dt)
+        dws = torch.empty(max(1, dws_n), dtype=torch.uint8, device=dev)
+        cargs = [(dt, wl.B, wl.Hkv, wl.D, ctypes.byref(kv), idx.data_ptr(), kmax, count.data_ptr(), kmax,
+                  ck.data_ptr(), cv.data_ptr(), max(1, kmax), sp) for kv in kvs]
+        ddargs = [(dqs[s].data_ptr(), dt, wl.B, wl.Hq, wl.Hkv, wl.D, ck.data_ptr(), cv.data_ptr(), max(1, kmax),
+                   count.data_ptr(), 0.0, douts[s].data_ptr(), dws.data_ptr(), dws_n, sp) for s in range(n_draft)]
+    f_compact, f_dense = L.sv_compact_kv, L.sv_dense_draft_attn
 
     def step(i, ev=None):
         c = i % copies
@@ -136,8 +159,13 @@ def main():
             f_hook(ev[0].cuda_event, ev[1].cuda_event)
         st = f_verify(*vargs[c])
         st |= f_topk(*targs)
-        for a in dargs[c]:
-            st |= f_sparse(*a)
+        if draft_path == "compact" and n_draft > 0:
+            st |= f_compact(*cargs[c])
+            for a in ddargs:
+                st |= f_dense(*a)
+        else:
+            for a in dargs[c]:
+                st |= f_sparse(*a)
         if st:
             raise RuntimeError(L.sv_last_error().decode())
 
@@ -238,7 +266,8 @@ def main():
         "config": {"workload": CONFIG_NAMES[args.workload], "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D,
                    "prefix": int(wl.P_max) if wl.B == 1 else [int(x) for x in wl.P], "verify_nodes": wl.N,
                    "tree": wl.parent is not None, "score_rows": len(rows), "k": int(wl.k_sel.max()),
-                   "draft_steps": n_draft, "paged": wl.layout == "paged", "kv_copies_rotated": copies,
+                   "draft_steps": n_draft, "draft_path": draft_path, "paged": wl.layout == "paged",
+                   "kv_copies_rotated": copies,
                    "step_bytes": step_bytes, "parallelism": "single-gpu"},
         "roofline": roof,
     }

@@ -9,7 +9,8 @@ At these sizes the oracle cannot run every attention row, so:
   * the selected index sets are compared whole against the oracle's selection
     from its own scores (tie-band rule);
   * the sparse draft step runs on the oracle's selected indices (an input from
-    the oracle side) and every output is compared.
+    the oracle side) and every output is compared; for several draft steps the
+    compacted path (rows gathered once, dense decodes) is compared as well.
 """
 import functools
 import time
@@ -89,10 +90,17 @@ def test_full_size_step(cfg):
     for b in range(wl.B):
         oi[b, : len(ref_idx[b])] = ref_idx[b]
     n = np.array([len(x) for x in ref_idx], np.int32)
+    compact = wl.dq.shape[0] > 1  # the benchmark's draft path for several draft steps
+    if compact:
+        cap = max(1, wl.k_max)
+        ck, cv = sv.compact_kv(dw.kv, i32(oi), i32(n), cap)
     for s in steps:
         d = sv.sparse_draft_attn(dw.dq[s], dw.kv, i32(oi), i32(n), max_idx=max(1, wl.k_max))
         dref = oracle.sparse_draft_attention(wl.dq[s], wl.dtype, kv, ref_idx, wl.scale, wl.Hkv)
         check_out(as_f64(d), dref, wl.dtype, f"draft step {s}")
+        if compact:
+            dd = sv.dense_draft_attn(dw.dq[s], ck, cv, i32(n))
+            check_out(as_f64(dd), dref, wl.dtype, f"compacted draft step {s}")
 
 
 @pytest.mark.parametrize("cfg", [2, 4])
