@@ -29,6 +29,8 @@ from .reference import (  # noqa: F401
     sparse_draft_attention,
     compact_kv,
     dense_draft_attention,
+    greedy_accept,
+    commit_accepted_kv,
     run_step,
     bf16_bits_to_f64,
 )

@@ -32,6 +32,10 @@ Pins (tests/test_oracle_*.py):
                           argmax) on tiny inputs with exact ties; golden cases
   sparse_draft_attention -- idx = whole prefix == dense decode; permutation
                           invariance; golden 2-key case
+  greedy_accept        -- chain closed form (leading matches); brute force on
+                          trees (the deepest node whose whole branch matches)
+  commit_accepted_kv   -- every moved row equals its source row, nothing else
+                          changes
   compact_kv, dense_draft_attention -- compacted rows == sparse_draft_attention
                           over the same list; a tail == the tail rows placed in
                           a cache past the prefix and listed; one row == its V
@@ -310,6 +314,45 @@ def dense_draft_attention(q1: np.ndarray, dtype: str, ck: np.ndarray, cv: np.nda
             hs = list(range(g * G, (g + 1) * G))
             out[b, hs] = _softmax_attend(scale * (Kg @ qf[b, hs].T), Vg)
     return out
+
+
+# ----------------------------------------------------------------------------
+# acceptance after verification and the accepted path's KV (Vegas §2: draft,
+# verify, accept; JETFLOW §2: a tree node's token is conditioned on its own
+# branch, so an accepted path is one root-to-node branch of the tree)
+
+def greedy_accept(parent: Optional[np.ndarray], draft: np.ndarray, target: np.ndarray) -> list[int]:
+    """Accepted path of one sequence, root first.  target[t] is the target
+    model's token after node t (its greedy choice); from the root, the path
+    moves to a child whose drafted token equals the target token at the
+    current node, the lowest-index one if several do, and stops when none does.
+    ``parent is None``: a linear chain."""
+    N = len(draft)
+    path = [0]
+    cur = 0
+    while True:
+        nxt = None
+        for c in range(cur + 1, N):
+            pc = (c - 1) if parent is None else int(parent[c])
+            if pc == cur and int(draft[c]) == int(target[cur]):
+                nxt = c
+                break
+        if nxt is None:
+            return path
+        path.append(nxt)
+        cur = nxt
+
+
+def commit_accepted_kv(kv: KVCache, b: int, P_b: int, path: Sequence[int]) -> None:
+    """Moves the accepted path's K/V rows to consecutive positions, in place on
+    kv.k / kv.v: after the call, logical position P_b + d holds the row that
+    position P_b + path[d] held before (d = 1 .. len(path) - 1; the root stays
+    at P_b).  The committed prefix then ends at P_b + len(path)."""
+    src = kv.slots(b, P_b + np.asarray(path[1:], dtype=np.int64))
+    dst = kv.slots(b, P_b + np.arange(1, len(path), dtype=np.int64))
+    krows, vrows = kv.k[src].copy(), kv.v[src].copy()
+    kv.k[dst] = krows
+    kv.v[dst] = vrows
 
 
 # ----------------------------------------------------------------------------

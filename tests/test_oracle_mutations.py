@@ -127,6 +127,34 @@ def test_compact_shifted_rows_is_caught(monkeypatch):
     assert _fails(pins.test_compacted_draft_equals_sparse_list, "bf16", "contiguous")
 
 
+def test_accept_compares_child_target_is_caught(monkeypatch):
+    def wrong(parent, draft, target):  # compares the child's drafted token with the child's own target
+        N = len(draft)
+        path, cur = [0], 0
+        while True:
+            nxt = None
+            for c in range(cur + 1, N):
+                pc = (c - 1) if parent is None else int(parent[c])
+                if pc == cur and int(draft[c]) == int(target[c]):
+                    nxt = c
+                    break
+            if nxt is None:
+                return path
+            path.append(nxt)
+            cur = nxt
+    _patch(monkeypatch, "greedy_accept", wrong)
+    assert _fails(pins.test_greedy_accept_golden)
+
+
+def test_commit_off_by_one_is_caught(monkeypatch):
+    orig = ref.commit_accepted_kv
+
+    def shifted(kv, b, P_b, path):
+        return orig(kv, b, P_b - 1, path)
+    _patch(monkeypatch, "commit_accepted_kv", shifted)
+    assert _fails(pins.test_commit_accepted_kv_moves_only_the_path)
+
+
 def test_unmutated_oracle_passes_the_same_checks():
     # the same check functions pass on the real oracle (guards against vacuous mutation tests)
     pins.test_golden_attention_three_keys()
@@ -135,3 +163,5 @@ def test_unmutated_oracle_passes_the_same_checks():
     pins.test_golden_topk_ties()
     pins.test_golden_sparse_two_keys()
     pins.test_compacted_draft_equals_sparse_list("bf16", "contiguous")
+    pins.test_greedy_accept_golden()
+    pins.test_commit_accepted_kv_moves_only_the_path()

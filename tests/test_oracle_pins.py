@@ -404,3 +404,64 @@ def test_dense_draft_single_row_permutation_and_empty():
     # no rows: zero output
     z = oracle.dense_draft_attention(wl.dq[0], "bf16", ck, cv, [0, 0], wl.scale, 2)
     assert (z == 0).all()
+
+
+# ----------------------------------------------------------------------------- acceptance
+
+def _branch_matched(parent, draft, target, v):
+    """Every edge on node v's root branch carries the target's token."""
+    while v != 0:
+        p = (v - 1) if parent is None else int(parent[v])
+        if int(draft[v]) != int(target[p]):
+            return False
+        v = p
+    return True
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_greedy_accept_brute_force(seed):
+    """On trees whose siblings carry distinct tokens, the accepted path is the
+    root branch of the deepest node whose whole branch matches (brute force
+    over every node); on chains, the leading run of matches."""
+    from workloads import best_first_tree, depth_logprobs, make_accept_tokens
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(2, 80))
+    parent = best_first_tree(N, depth_logprobs(rng, 6), 6)[0][None]
+    draft, target = make_accept_tokens(seed, parent, match_prob=float(rng.uniform(0.3, 1.0)))
+    path = oracle.greedy_accept(parent[0], draft[0], target[0])
+    matched = [v for v in range(N) if _branch_matched(parent[0], draft[0], target[0], v)]
+    deepest = max(matched, key=lambda v: (len(oracle.ancestors(parent[0], v)), -v))
+    assert path == sorted(oracle.ancestors(parent[0], deepest))
+    # chain: leading matches
+    chain = np.arange(-1, N - 1, dtype=np.int32)[None]
+    d2, t2 = make_accept_tokens(seed + 100, chain, match_prob=0.8)
+    n_lead = 0
+    while n_lead + 1 < N and d2[0, n_lead + 1] == t2[0, n_lead]:
+        n_lead += 1
+    assert oracle.greedy_accept(None, d2[0], t2[0]) == list(range(n_lead + 1))
+    assert oracle.greedy_accept(chain[0], d2[0], t2[0]) == list(range(n_lead + 1))
+
+
+def test_greedy_accept_golden():
+    # root 0 -> {1, 2}; 1 -> {3}; 2 -> {4, 5}.  Target after 0 is token 20 (node 2),
+    # after 2 is 51 (node 5), after 5 nothing matches.
+    parent = np.array([-1, 0, 0, 1, 2, 2])
+    draft = np.array([7, 10, 20, 30, 50, 51])
+    target = np.array([20, 30, 51, 0, 0, 99])
+    assert oracle.greedy_accept(parent, draft, target) == [0, 2, 5]
+    # nothing accepted: the path is the root alone
+    assert oracle.greedy_accept(parent, draft, np.array([5, 0, 0, 0, 0, 0])) == [0]
+
+
+def test_commit_accepted_kv_moves_only_the_path():
+    wl = make_custom(seed=31, dtype="bf16", B=2, Hq=4, Hkv=2, D=64, P=[40, 25], N=8)
+    kv = KVCache.of(wl)
+    k0, v0 = wl.k.copy(), wl.v.copy()
+    path = [0, 2, 5, 7]
+    oracle.commit_accepted_kv(kv, 1, 25, path)
+    for d in range(1, 4):
+        assert np.array_equal(wl.k[kv.slots(1, [25 + d])], k0[kv.slots(1, [25 + path[d]])])
+        assert np.array_equal(wl.v[kv.slots(1, [25 + d])], v0[kv.slots(1, [25 + path[d]])])
+    moved = set(kv.slots(1, 25 + np.arange(1, 4)).tolist())
+    other = [s for s in range(wl.k.shape[0]) if s not in moved]
+    assert np.array_equal(wl.k[other], k0[other]) and np.array_equal(wl.v[other], v0[other])

@@ -23,6 +23,7 @@ from .gen import (  # noqa: F401
     make_custom,
     make_score_vector,
     make_tail_rows,
+    make_accept_tokens,
     CONFIG_NAMES,
     bf16_bits_from_f32,
     f32_from_bf16_bits,

@@ -33,7 +33,7 @@ import numpy as np
 from .tree import best_first_tree, chain_parents, depth_logprobs
 
 # generator stream ids (one stream per tensor)
-_S_Q, _S_K, _S_V, _S_HEAVY, _S_TREE, _S_DQ, _S_LEN, _S_PAGES, _S_SCORES, _S_TAIL = range(10)
+_S_Q, _S_K, _S_V, _S_HEAVY, _S_TREE, _S_DQ, _S_LEN, _S_PAGES, _S_SCORES, _S_TAIL, _S_ACCEPT = range(11)
 
 CONFIG_NAMES = {
     1: "tiny-fp32-chain-p512",
@@ -320,6 +320,39 @@ def make_tail_rows(seed, steps: int, B: int, Hkv: int, D: int, dtype: str) -> tu
     k = _draw(r, (steps, B, Hkv, D), sd)
     v = _draw(r, (steps, B, Hkv, D), sd)
     return _store(k, dtype), _store(v, dtype)
+
+
+def make_accept_tokens(seed, parent: np.ndarray, match_prob: float = 0.75,
+                       vocab: int = 32000) -> tuple[np.ndarray, np.ndarray]:
+    """Synthetic drafted and target tokens for acceptance on draft trees.
+
+    parent: int32 [B][N].  Drafted token of a node: distinct among siblings (a
+    child's rank among its parent's children, offset by a per-parent random
+    base, as the per-depth candidate lists of the tree generator give).
+    Target token at a node: with probability ``match_prob`` the drafted token of
+    one of its children (drawn uniformly), otherwise a token no drafted node
+    carries (>= vocab).  Returns (draft, target), int32 [B][N] each."""
+    r = np.random.default_rng([int(x) for x in np.atleast_1d(seed)] + [_S_ACCEPT])
+    parent = np.asarray(parent, dtype=np.int32)
+    B, N = parent.shape
+    draft = np.zeros((B, N), dtype=np.int32)
+    target = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        base = r.integers(0, vocab // 2, size=N)
+        nkids = np.zeros(N, dtype=np.int64)
+        kids = [[] for _ in range(N)]
+        draft[b, 0] = int(r.integers(0, vocab))
+        for t in range(1, N):
+            p = int(parent[b, t])
+            draft[b, t] = int((base[p] + nkids[p]) % vocab)
+            nkids[p] += 1
+            kids[p].append(t)
+        for t in range(N):
+            if kids[t] and r.random() < match_prob:
+                target[b, t] = draft[b, kids[t][int(r.integers(0, len(kids[t])))]]
+            else:
+                target[b, t] = vocab + int(r.integers(0, vocab))
+    return draft, target
 
 
 def make_score_vector(seed: int, n: int, kind: str = "normal") -> np.ndarray:
