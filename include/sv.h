@@ -16,6 +16,8 @@
  *   sv_compact_kv, sv_dense_draft_attn   the same draft steps over the set
  *                         gathered once into dense buffers, plus a tail of
  *                         drafted tokens' rows.
+ *   sv_accept_commit      greedy acceptance of the verified drafts and the
+ *                         accepted branch's K/V moved behind the prefix.
  *
  * Sources (technical-summary pages on gist.science/pt/paper/...):
  *   Vegas (2602.07223): §2 "Mecanismo Central" steps 1-3 (verify with full
@@ -212,6 +214,41 @@ sv_status sv_dense_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int 
                               const void* ck, const void* cv, int cap, const int32_t* n_rows,
                               float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                               sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Acceptance after verification and the accepted path's KV (Vegas §2: draft,
+ * verify, accept; JETFLOW §2: a drafted node is conditioned on its own branch,
+ * so what is accepted is one root-to-node branch of the tree).
+ *
+ * Greedy acceptance: target_tokens[b][t] is the target model's token after
+ * node t (its argmax at verify row t).  From the root, the path moves to the
+ * child whose drafted token equals the target token at the current node (the
+ * lowest-index child if several do) and stops when no child does.  Then, when
+ * kv is non-NULL, the K/V rows of the path are moved IN PLACE to consecutive
+ * positions: position P_b + d receives the row of position P_b + path[d]
+ * (d >= 1; the root stays at P_b), all KV heads, bytes unchanged.  The
+ * committed prefix then ends at P_b + path length; the bonus token (the target
+ * token at the path's last node) is the next token to decode.
+ *
+ *   dtype, Hkv, D    row format of the cache (ignored when kv is NULL).
+ *   kv               the cache to update, or NULL for acceptance only.  This
+ *                    call WRITES kv->k and kv->v (the rows P_b + 1 .. P_b + d).
+ *   prefix_len       device int32[B] P_b (clamped to [0, P_max]); may be NULL
+ *                    only when kv and new_prefix_len are NULL.
+ *   parent           device int32[B][N] tree parents, or NULL for a chain.
+ *   draft_tokens     device int32[B][N]: the drafted token of each node (the
+ *                    root's entry is not read).
+ *   target_tokens    device int32[B][N].
+ *   path             device int32[B][N] out: path node ids by depth, root
+ *                    first, then -1.
+ *   n_accepted       device int32[B] out: accepted drafted nodes (path length - 1).
+ *   bonus            device int32[B] out, or NULL.
+ *   new_prefix_len   device int32[B] out, or NULL: P_b + path length.
+ */
+sv_status sv_accept_commit(sv_dtype dtype, int B, int N, int Hkv, int D, const sv_kv_cache* kv,
+                           const int32_t* prefix_len, int P_max, const int32_t* parent,
+                           const int32_t* draft_tokens, const int32_t* target_tokens, int32_t* path,
+                           int32_t* n_accepted, int32_t* bonus, int32_t* new_prefix_len, sv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* Optional timing hook for profiling: while set (non-NULL), every

@@ -153,6 +153,23 @@ def test_compact_and_dense_draft_reject_bad_arguments():
     assert dd(None, _lib.SV_BF16, 0, 32, 8, 128, None, None, 4096, None, 0.0, None, None, 0, None) == _lib.SV_OK
 
 
+def test_accept_commit_rejects_bad_arguments():
+    lib = _lib.load()
+    kv = _kv()
+    ac = lib.sv_accept_commit
+
+    def call(B=1, N=8, kvp=ctypes.byref(kv), P=FAKE, draft=FAKE, target=FAKE, path=FAKE, nacc=FAKE, newp=FAKE, D=128):
+        return ac(_lib.SV_BF16, B, N, 8, D, kvp, P, 100, None, draft, target, path, nacc, None, newp, None)
+    assert call(N=0) == _lib.SV_E_INVALID
+    assert call(N=257) == _lib.SV_E_UNSUPPORTED
+    assert call(D=96) == _lib.SV_E_UNSUPPORTED
+    assert call(draft=None) == _lib.SV_E_INVALID
+    assert call(path=None) == _lib.SV_E_INVALID
+    assert call(P=None) == _lib.SV_E_INVALID                      # the K/V move needs P_b
+    assert "prefix_len" in lib.sv_last_error().decode()
+    assert call(B=0, draft=None, target=None, path=None, nacc=None) == _lib.SV_OK
+
+
 def test_timing_events_must_pair():
     lib = _lib.load()
     assert lib.sv_set_verify_timing_events(FAKE, None) == _lib.SV_E_INVALID

@@ -25,7 +25,7 @@ from ._lib import SvError, SV_F32, SV_BF16  # noqa: F401
 
 __all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn", "compact_kv",
            "dense_draft_attn", "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size",
-           "dense_draft_workspace_size", "timing_events", "SvError", "lib"]
+           "dense_draft_workspace_size", "accept_commit", "timing_events", "SvError", "lib"]
 
 
 def lib() -> ctypes.CDLL:
@@ -228,6 +228,27 @@ def dense_draft_attn(q: torch.Tensor, ck: torch.Tensor, cv: torch.Tensor, n_rows
     _lib.check(L.sv_dense_draft_attn(_ptr(q), dt, B, Hq, Hkv, D, _ptr(ck), _ptr(cv), cap, _ptr(n_rows),
                                      float(scale), _ptr(out), wptr, wlen, _stream(q.device)))
     return out
+
+
+def accept_commit(draft_tokens: torch.Tensor, target_tokens: torch.Tensor, *, parent: Optional[torch.Tensor] = None,
+                  kv: Optional[KVCache] = None, prefix_len: Optional[torch.Tensor] = None, P_max: int = 0):
+    """sv_accept_commit: greedy acceptance (and, with kv, the accepted branch's
+    K/V moved in place behind the prefix).  Returns (path int32 [B][N],
+    n_accepted int32 [B], bonus int32 [B], new_prefix_len int32 [B] or None)."""
+    L = lib()
+    B, N = (int(x) for x in draft_tokens.shape)
+    dev = draft_tokens.device
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    new_p = torch.empty((B,), dtype=torch.int32, device=dev) if prefix_len is not None else None
+    kvs = kv.c_struct() if kv is not None else None
+    dt = _dtype_code(kv.k) if kv is not None else SV_BF16
+    _lib.check(L.sv_accept_commit(dt, B, N, kv.Hkv if kv is not None else 1, kv.D if kv is not None else 128,
+                                  ctypes.byref(kvs) if kvs is not None else None, _ptr(prefix_len), int(P_max),
+                                  _ptr(parent), _ptr(draft_tokens), _ptr(target_tokens), _ptr(path), _ptr(n_acc),
+                                  _ptr(bonus), _ptr(new_p), _stream(dev)))
+    return path, n_acc, bonus, new_p
 
 
 class timing_events:

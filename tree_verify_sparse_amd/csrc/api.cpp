@@ -225,4 +225,31 @@ sv_status sv_dense_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int 
   return hip_status(e, "sv_dense_draft_attn launch");
 }
 
+sv_status sv_accept_commit(sv_dtype dtype, int B, int N, int Hkv, int D, const sv_kv_cache* kv,
+                           const int32_t* prefix_len, int P_max, const int32_t* parent, const int32_t* draft_tokens,
+                           const int32_t* target_tokens, int32_t* path, int32_t* n_accepted, int32_t* bonus,
+                           int32_t* new_prefix_len, sv_stream stream) {
+  sv_status st;
+  if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
+  if (N <= 0) return fail(SV_E_INVALID, "N must be >= 1");
+  if (N > sv::kMaxNodes) return fail(SV_E_UNSUPPORTED, "N = %d draft nodes exceeds %d", N, sv::kMaxNodes);
+  if (P_max < 0) return fail(SV_E_INVALID, "P_max must be >= 0");
+  if (kv) {
+    if ((st = check_dtype(dtype))) return st;
+    if ((st = check_heads(Hkv, Hkv, D))) return st;
+  }
+  if (B == 0) return ok();
+  if (!draft_tokens || !target_tokens || !path || !n_accepted)
+    return fail(SV_E_INVALID, "draft_tokens, target_tokens, path and n_accepted must be non-NULL");
+  if ((kv || new_prefix_len) && !prefix_len) return fail(SV_E_INVALID, "prefix_len is NULL");
+  sv::KvArgs ka{};
+  if (kv) {
+    if ((st = check_kv(kv, B))) return st;
+    ka = kv_args(kv);
+  }
+  return hip_status(sv::launch_accept((int)dtype, B, N, Hkv, D, kv ? &ka : nullptr, prefix_len, P_max, parent,
+                                      draft_tokens, target_tokens, path, n_accepted, bonus, new_prefix_len, stream),
+                    "sv_accept_commit launch");
+}
+
 }  // extern "C"

@@ -58,6 +58,10 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
                   void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
                   int len_bias = 0);
+// Greedy acceptance on draft trees and the accepted path's K/V move (kv may be null).
+int launch_accept(int dtype, int B, int N, int Hkv, int D, const KvArgs* kv, const int32_t* prefix_len, int P_max,
+                  const int32_t* parent, const int32_t* draft, const int32_t* target, int32_t* path,
+                  int32_t* n_accepted, int32_t* bonus, int32_t* new_prefix, void* stream);
 // Gather the listed rows (all KV heads) into dense [B][cap][Hkv][D] buffers.
 int launch_compact(int dtype, int B, int Hkv, int D, const KvArgs& kv, const int32_t* idx, int idx_stride,
                    const int32_t* n_idx, int max_idx, void* ck, void* cv, int cap, void* stream);
