@@ -254,6 +254,32 @@ def main():
     roof["algorithmic_flops"] = verify_flops
     roof["traffic"] = _traffic(args.workload)
 
+    # after the timed passes: acceptance of this workload's drafts with the
+    # accepted branch's K/V moved in place, on KV copy 0.  Synthetic target
+    # tokens always match some child, so every path runs to a leaf (the
+    # longest walks and the most row moves)
+    from workloads import make_accept_tokens
+    par_np = wl.parent if wl.parent is not None else np.tile(np.arange(-1, wl.N - 1, dtype=np.int32), (wl.B, 1))
+    d_tok, t_tok = make_accept_tokens([args.workload, args.seed], par_np, match_prob=1.0)
+    d_tok, t_tok = i32(d_tok), i32(t_tok)
+    apath = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
+    an = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    abonus = torch.empty_like(an)
+    anewp = torch.empty_like(an)
+    aargs = (dt, wl.B, wl.N, wl.Hkv, wl.D, ctypes.byref(kvs[0]), P.data_ptr(), wl.P_max,
+             parent.data_ptr() if parent is not None else None, d_tok.data_ptr(), t_tok.data_ptr(), apath.data_ptr(),
+             an.data_ptr(), abonus.data_ptr(), anewp.data_ptr(), sp)
+    for _ in range(3):
+        L.sv_accept_commit(*aargs)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        if L.sv_accept_commit(*aargs):
+            raise RuntimeError(L.sv_last_error().decode())
+    e1.record()
+    torch.cuda.synchronize()
+    accept_us = e0.elapsed_time(e1) * 1e3 / K
+
     value = step_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": "verify+select+sparse-draft us/step and HBM GB/s (% peak) at 32k ctx, 1 GPU",
@@ -270,6 +296,8 @@ def main():
                    "kv_copies_rotated": copies,
                    "step_bytes": step_bytes, "parallelism": "single-gpu"},
         "roofline": roof,
+        "next_rows": {"accept_commit_us": round(accept_us, 2),
+                      "accepted_mean": round(float(an.float().mean().item()), 2)},
     }
     if not args.no_cpu_baseline and args.workload in (1, 2, 3):
         res["cpu_baseline"] = cpu_baseline(wl, step_bytes, args.cpu_seconds)
