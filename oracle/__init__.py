@@ -29,6 +29,7 @@ from .reference import (  # noqa: F401
     sparse_draft_attention,
     compact_kv,
     dense_draft_attention,
+    build_best_first_tree,
     greedy_accept,
     commit_accepted_kv,
     run_step,

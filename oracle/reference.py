@@ -32,6 +32,9 @@ Pins (tests/test_oracle_*.py):
                           argmax) on tiny inputs with exact ties; golden cases
   sparse_draft_attention -- idx = whole prefix == dense decode; permutation
                           invariance; golden 2-key case
+  build_best_first_tree -- brute force: node i is the i-th best of every node
+                          reachable within the depth limit; golden tie order;
+                          equal to the input generator's trees
   greedy_accept        -- chain closed form (leading matches); brute force on
                           trees (the deepest node whose whole branch matches)
   commit_accepted_kv   -- every moved row equals its source row, nothing else
@@ -314,6 +317,41 @@ def dense_draft_attention(q1: np.ndarray, dtype: str, ck: np.ndarray, cv: np.nda
             hs = list(range(g * G, (g + 1) * G))
             out[b, hs] = _softmax_attend(scale * (Kg @ qf[b, hs].T), Vg)
     return out
+
+
+# ----------------------------------------------------------------------------
+# draft tree construction (JETFLOW §2, tree construction: the draft head gives
+# log-probabilities for every depth at once, a branch is scored by its
+# cumulative draft log-probability, and best-first expansion grows the tree up
+# to a node budget)
+
+def build_best_first_tree(lp: np.ndarray, n_nodes: int, max_depth: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """lp: float64 [max_depth + 1][n_cand], row d the candidate log-probs at
+    depth d in decreasing order (row 0 unused).  Node 0 is the root.  A
+    candidate is (parent node, rank) at depth(parent) + 1 with score
+    cum(parent) + lp[depth][rank]; the best candidate (highest score, then
+    lower parent id, then lower rank) becomes the next node.  A new node offers
+    its rank-0 child; a taken candidate offers its parent's next rank (the
+    lists are sorted, so the untaken ranks of a parent are never better than
+    the next one).  Returns (parent, depth, rank), int32 [n_nodes] each."""
+    n_cand = lp.shape[1]
+    parent, depth, rank, cum = [-1], [0], [0], [0.0]
+    cands = []  # (score, parent, rank, depth)
+    if n_nodes > 1 and max_depth >= 1:
+        cands.append((0.0 + float(lp[1][0]), 0, 0, 1))
+    while len(parent) < n_nodes:
+        best = min(range(len(cands)), key=lambda j: (-cands[j][0], cands[j][1], cands[j][2]))
+        sc, p, r, d = cands.pop(best)
+        i = len(parent)
+        parent.append(p)
+        depth.append(d)
+        rank.append(r)
+        cum.append(sc)
+        if d < max_depth:
+            cands.append((sc + float(lp[d + 1][0]), i, 0, d + 1))
+        if r + 1 < n_cand:
+            cands.append((cum[p] + float(lp[d][r + 1]), p, r + 1, d))
+    return (np.asarray(parent, dtype=np.int32), np.asarray(depth, dtype=np.int32), np.asarray(rank, dtype=np.int32))
 
 
 # ----------------------------------------------------------------------------

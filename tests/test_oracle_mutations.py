@@ -155,6 +155,43 @@ def test_commit_off_by_one_is_caught(monkeypatch):
     assert _fails(pins.test_commit_accepted_kv_moves_only_the_path)
 
 
+def test_tree_builder_ties_to_higher_parent_is_caught(monkeypatch):
+    def wrong(lp, n_nodes, max_depth):  # same expansion, ties broken toward the higher parent id
+        n_cand = lp.shape[1]
+        parent, depth, rank, cum = [-1], [0], [0], [0.0]
+        cands = [(float(lp[1][0]), 0, 0, 1)] if n_nodes > 1 and max_depth >= 1 else []
+        while len(parent) < n_nodes:
+            best = min(range(len(cands)), key=lambda j: (-cands[j][0], -cands[j][1], cands[j][2]))
+            sc, p, r, d = cands.pop(best)
+            i = len(parent)
+            parent.append(p), depth.append(d), rank.append(r), cum.append(sc)
+            if d < max_depth:
+                cands.append((sc + float(lp[d + 1][0]), i, 0, d + 1))
+            if r + 1 < n_cand:
+                cands.append((cum[p] + float(lp[d][r + 1]), p, r + 1, d))
+        return tuple(np.asarray(x, dtype=np.int32) for x in (parent, depth, rank))
+    _patch(monkeypatch, "build_best_first_tree", wrong)
+    assert _fails(pins.test_best_first_tree_golden_ties_and_generator)
+
+
+def test_tree_builder_without_sibling_offers_is_caught(monkeypatch):
+    def wrong(lp, n_nodes, max_depth):  # a taken candidate does not offer the next rank
+        parent, depth, rank, cum = [-1], [0], [0], [0.0]
+        cands = [(float(lp[1][0]), 0, 0, 1)] if n_nodes > 1 and max_depth >= 1 else []
+        while len(parent) < n_nodes and cands:
+            best = min(range(len(cands)), key=lambda j: (-cands[j][0], cands[j][1], cands[j][2]))
+            sc, p, r, d = cands.pop(best)
+            i = len(parent)
+            parent.append(p), depth.append(d), rank.append(r), cum.append(sc)
+            if d < max_depth:
+                cands.append((sc + float(lp[d + 1][0]), i, 0, d + 1))
+        while len(parent) < n_nodes:
+            parent.append(0), depth.append(1), rank.append(0)
+        return tuple(np.asarray(x, dtype=np.int32) for x in (parent, depth, rank))
+    _patch(monkeypatch, "build_best_first_tree", wrong)
+    assert any(_fails(pins.test_best_first_tree_brute_force, seed) for seed in range(10))
+
+
 def test_unmutated_oracle_passes_the_same_checks():
     # the same check functions pass on the real oracle (guards against vacuous mutation tests)
     pins.test_golden_attention_three_keys()
@@ -164,4 +201,5 @@ def test_unmutated_oracle_passes_the_same_checks():
     pins.test_golden_sparse_two_keys()
     pins.test_compacted_draft_equals_sparse_list("bf16", "contiguous")
     pins.test_greedy_accept_golden()
+    pins.test_best_first_tree_golden_ties_and_generator()
     pins.test_commit_accepted_kv_moves_only_the_path()

@@ -465,3 +465,59 @@ def test_commit_accepted_kv_moves_only_the_path():
     moved = set(kv.slots(1, 25 + np.arange(1, 4)).tolist())
     other = [s for s in range(wl.k.shape[0]) if s not in moved]
     assert np.array_equal(wl.k[other], k0[other]) and np.array_equal(wl.v[other], v0[other])
+
+
+# ----------------------------------------------------------------------------- tree construction
+
+def _all_nodes(lp, max_depth):
+    """Every node reachable within the depth limit: (score, rank path)."""
+    out = []
+
+    def rec(path, score):
+        d = len(path)
+        if d == max_depth:
+            return
+        for r in range(lp.shape[1]):
+            sc = score + lp[d + 1][r]
+            out.append((sc, path + (r,)))
+            rec(path + (r,), sc)
+    rec((), 0.0)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_best_first_tree_brute_force(seed):
+    """Node i (i >= 1) is the i-th best of all reachable nodes (scores are
+    continuous, so there are no ties), and its parent is the node of the same
+    rank path minus its last step."""
+    rng = np.random.default_rng(seed)
+    n_cand, max_depth = int(rng.integers(2, 5)), int(rng.integers(1, 4))
+    lp = np.zeros((max_depth + 1, n_cand))
+    for d in range(1, max_depth + 1):
+        z = rng.normal(0, np.sqrt(2), n_cand)
+        lp[d] = np.sort(z - np.log(np.exp(z).sum()))[::-1]
+    allnodes = sorted(_all_nodes(lp, max_depth), key=lambda x: -x[0])
+    n = int(rng.integers(1, min(len(allnodes) + 1, 40) + 1))
+    parent, depth, rank = oracle.build_best_first_tree(lp, n, max_depth)
+    paths = {(): 0}
+    for i in range(1, n):
+        sc, path = allnodes[i - 1]
+        paths[path] = i
+        assert parent[i] == paths[path[:-1]], f"node {i}"
+        assert depth[i] == len(path) and rank[i] == path[-1]
+
+
+def test_best_first_tree_golden_ties_and_generator():
+    # two candidate lists with equal entries: ties go to the lower parent id, then the lower rank
+    lp = np.array([[0.0, 0.0], [-1.0, -1.0], [-1.0, -2.0]])
+    parent, depth, rank = oracle.build_best_first_tree(lp, 5, 2)
+    # root -> (0, r0) -1 -> (0, r1) -1 [tie: lower rank first] -> child of node 1 r0: -2, child of node 2 r0: -2
+    assert parent.tolist() == [-1, 0, 0, 1, 2] and rank.tolist() == [0, 0, 1, 0, 0] and depth.tolist() == [0, 1, 1, 2, 2]
+    # the input generator's trees (configs 3 and 5 shapes) are the same trees
+    from workloads import best_first_tree, depth_logprobs
+    for seed, n, dmax in ((1, 256, 8), (2, 64, 6), (3, 100, 3)):
+        lpg = depth_logprobs(np.random.default_rng(seed), dmax)
+        g = best_first_tree(n, lpg, dmax)
+        o = oracle.build_best_first_tree(lpg, n, dmax)
+        for a, b in zip(g, o):
+            assert np.array_equal(a, b)
