@@ -16,6 +16,8 @@
  *   sv_compact_kv, sv_dense_draft_attn   the same draft steps over the set
  *                         gathered once into dense buffers, plus a tail of
  *                         drafted tokens' rows.
+ *   sv_build_tree         best-first draft tree (parent array) from per-depth
+ *                         draft log-probabilities.
  *   sv_accept_commit      greedy acceptance of the verified drafts and the
  *                         accepted branch's K/V moved behind the prefix.
  *
@@ -214,6 +216,31 @@ sv_status sv_dense_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int 
                               const void* ck, const void* cv, int cap, const int32_t* n_rows,
                               float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                               sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Best-first draft tree construction (JETFLOW §2, tree construction: the
+ * draft head gives log-probabilities for every depth at once, a branch is
+ * scored by its cumulative draft log-probability, and best-first expansion
+ * grows the tree up to a node budget), on the device so the parent array feeds
+ * sv_verify_attn without a host round trip.
+ *
+ * Node 0 is the root.  A candidate (parent node v, rank r) sits at depth
+ * depth(v) + 1 with score score(v) + logprobs[b][depth][r] (fp64, the root
+ * scoring 0).  Repeatedly the best candidate -- highest score, then lower
+ * parent id, then lower rank -- becomes the next node; a new node offers its
+ * rank-0 child (within max_depth) and a taken candidate offers its parent's
+ * next rank.  Nodes are numbered in that order, so parents precede children.
+ *
+ *   logprobs   device fp64 [B][max_depth + 1][n_cand]; row d holds depth d's
+ *              candidate log-probabilities in decreasing order (row 0 unused).
+ *   n_nodes    node budget including the root, 1..256; it must not exceed
+ *              the nodes reachable with n_cand ranks per depth (checked).
+ *   n_cand     1..256.
+ *   parent     device int32[B][n_nodes] out (parent[b][0] = -1).
+ *   depth, rank   device int32[B][n_nodes] out, or NULL.
+ */
+sv_status sv_build_tree(int B, int n_nodes, int max_depth, int n_cand, const double* logprobs,
+                        int32_t* parent, int32_t* depth, int32_t* rank, sv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* Acceptance after verification and the accepted path's KV (Vegas §2: draft,

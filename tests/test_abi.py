@@ -170,6 +170,19 @@ def test_accept_commit_rejects_bad_arguments():
     assert call(B=0, draft=None, target=None, path=None, nacc=None) == _lib.SV_OK
 
 
+def test_build_tree_rejects_bad_arguments():
+    lib = _lib.load()
+    bt = lib.sv_build_tree
+    assert bt(1, 0, 8, 32, FAKE, FAKE, None, None, None) == _lib.SV_E_INVALID
+    assert bt(1, 257, 8, 32, FAKE, FAKE, None, None, None) == _lib.SV_E_UNSUPPORTED
+    assert bt(1, 16, 8, 300, FAKE, FAKE, None, None, None) == _lib.SV_E_UNSUPPORTED
+    assert bt(1, 16, 2, 3, FAKE, FAKE, None, None, None) == _lib.SV_E_INVALID     # 1 + 3 + 9 = 13 reachable
+    assert "reachable" in lib.sv_last_error().decode()
+    assert bt(1, 2, 0, 32, FAKE, FAKE, None, None, None) == _lib.SV_E_INVALID     # depth 0: only the root
+    assert bt(1, 16, 8, 32, None, FAKE, None, None, None) == _lib.SV_E_INVALID
+    assert bt(0, 16, 8, 32, None, None, None, None, None) == _lib.SV_OK
+
+
 def test_timing_events_must_pair():
     lib = _lib.load()
     assert lib.sv_set_verify_timing_events(FAKE, None) == _lib.SV_E_INVALID

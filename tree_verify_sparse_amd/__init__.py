@@ -25,7 +25,7 @@ from ._lib import SvError, SV_F32, SV_BF16  # noqa: F401
 
 __all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn", "compact_kv",
            "dense_draft_attn", "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size",
-           "dense_draft_workspace_size", "accept_commit", "timing_events", "SvError", "lib"]
+           "dense_draft_workspace_size", "build_tree", "accept_commit", "timing_events", "SvError", "lib"]
 
 
 def lib() -> ctypes.CDLL:
@@ -228,6 +228,22 @@ def dense_draft_attn(q: torch.Tensor, ck: torch.Tensor, cv: torch.Tensor, n_rows
     _lib.check(L.sv_dense_draft_attn(_ptr(q), dt, B, Hq, Hkv, D, _ptr(ck), _ptr(cv), cap, _ptr(n_rows),
                                      float(scale), _ptr(out), wptr, wlen, _stream(q.device)))
     return out
+
+
+def build_tree(logprobs: torch.Tensor, n_nodes: int):
+    """sv_build_tree: logprobs fp64 [B][max_depth + 1][n_cand] (rows sorted
+    decreasing) -> (parent, depth, rank), int32 [B][n_nodes] each."""
+    L = lib()
+    if logprobs.dtype != torch.float64 or logprobs.dim() != 3:
+        raise ValueError("logprobs must be float64 [B][max_depth + 1][n_cand]")
+    B, md1, nc = (int(x) for x in logprobs.shape)
+    dev = logprobs.device
+    parent = torch.empty((B, n_nodes), dtype=torch.int32, device=dev)
+    depth = torch.empty_like(parent)
+    rank = torch.empty_like(parent)
+    _lib.check(L.sv_build_tree(B, int(n_nodes), md1 - 1, nc, _ptr(logprobs), _ptr(parent), _ptr(depth), _ptr(rank),
+                               _stream(dev)))
+    return parent, depth, rank
 
 
 def accept_commit(draft_tokens: torch.Tensor, target_tokens: torch.Tensor, *, parent: Optional[torch.Tensor] = None,

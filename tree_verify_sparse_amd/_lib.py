@@ -16,7 +16,8 @@ EXPORTS = (
     "sv_verify_workspace_size", "sv_verify_attn",
     "sv_topk_workspace_size", "sv_topk_select",
     "sv_sparse_workspace_size", "sv_sparse_draft_attn",
-    "sv_compact_kv", "sv_dense_draft_workspace_size", "sv_dense_draft_attn", "sv_accept_commit",
+    "sv_compact_kv", "sv_dense_draft_workspace_size", "sv_dense_draft_attn", "sv_build_tree",
+    "sv_accept_commit",
     "sv_set_verify_timing_events",
 )
 
@@ -77,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.sv_dense_draft_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.sv_dense_draft_attn.restype = i32
     lib.sv_dense_draft_attn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, f32, vp, vp, sz, vp]
+    lib.sv_build_tree.restype = i32
+    lib.sv_build_tree.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.sv_accept_commit.restype = i32
     lib.sv_accept_commit.argtypes = [i32, i32, i32, i32, i32, kvp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sv_set_verify_timing_events.restype = i32

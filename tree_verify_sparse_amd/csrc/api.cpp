@@ -252,4 +252,26 @@ sv_status sv_accept_commit(sv_dtype dtype, int B, int N, int Hkv, int D, const s
                     "sv_accept_commit launch");
 }
 
+sv_status sv_build_tree(int B, int n_nodes, int max_depth, int n_cand, const double* logprobs, int32_t* parent,
+                        int32_t* depth, int32_t* rank, sv_stream stream) {
+  if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
+  if (n_nodes < 1) return fail(SV_E_INVALID, "n_nodes must be >= 1");
+  if (n_nodes > sv::kMaxNodes) return fail(SV_E_UNSUPPORTED, "n_nodes = %d exceeds %d", n_nodes, sv::kMaxNodes);
+  if (n_cand < 1 || n_cand > 256) return fail(SV_E_UNSUPPORTED, "n_cand = %d not in [1, 256]", n_cand);
+  if (max_depth < 0) return fail(SV_E_INVALID, "max_depth must be >= 0");
+  // nodes reachable within the depth limit (saturating): the budget must fit
+  long long reach = 1, level = 1;
+  for (int d = 1; d <= max_depth && reach < n_nodes; ++d) {
+    level = level * n_cand > (1LL << 20) ? (1LL << 20) : level * n_cand;
+    reach += level;
+  }
+  if (reach < n_nodes)
+    return fail(SV_E_INVALID, "only %lld nodes are reachable with n_cand = %d and max_depth = %d", reach, n_cand,
+                max_depth);
+  if (B == 0) return ok();
+  if (!logprobs || !parent) return fail(SV_E_INVALID, "logprobs and parent must be non-NULL");
+  return hip_status(sv::launch_build_tree(B, n_nodes, max_depth, n_cand, logprobs, parent, depth, rank, stream),
+                    "sv_build_tree launch");
+}
+
 }  // extern "C"

@@ -58,6 +58,9 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
                   void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
                   int len_bias = 0);
+// Best-first draft trees from per-depth log-probabilities (one wave per sequence).
+int launch_build_tree(int B, int n, int max_depth, int n_cand, const double* lp, int32_t* parent, int32_t* depth,
+                      int32_t* rank, void* stream);
 // Greedy acceptance on draft trees and the accepted path's K/V move (kv may be null).
 int launch_accept(int dtype, int B, int N, int Hkv, int D, const KvArgs* kv, const int32_t* prefix_len, int P_max,
                   const int32_t* parent, const int32_t* draft, const int32_t* target, int32_t* path,
