@@ -279,6 +279,26 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     accept_us = e0.elapsed_time(e1) * 1e3 / K
+    # device tree construction for tree workloads: this workload's tree shape
+    # from seeded per-depth log-probabilities (the same generator as its trees)
+    build_us = None
+    if wl.parent is not None:
+        from workloads import depth_logprobs
+        dmax = {3: 8, 5: 6}.get(args.workload, 8)
+        r = np.random.default_rng([args.workload, args.seed, 99])
+        lps = torch.from_numpy(np.stack([depth_logprobs(r, dmax) for _ in range(wl.B)])).to(dev)
+        bt_par = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
+        bargs = (wl.B, wl.N, dmax, int(lps.shape[2]), lps.data_ptr(), bt_par.data_ptr(), None, None, sp)
+        for _ in range(3):
+            L.sv_build_tree(*bargs)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            if L.sv_build_tree(*bargs):
+                raise RuntimeError(L.sv_last_error().decode())
+        e1.record()
+        torch.cuda.synchronize()
+        build_us = e0.elapsed_time(e1) * 1e3 / K
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     res = {
@@ -297,7 +317,8 @@ def main():
                    "step_bytes": step_bytes, "parallelism": "single-gpu"},
         "roofline": roof,
         "next_rows": {"accept_commit_us": round(accept_us, 2),
-                      "accepted_mean": round(float(an.float().mean().item()), 2)},
+                      "accepted_mean": round(float(an.float().mean().item()), 2),
+                      "build_tree_us": round(build_us, 2) if build_us is not None else None},
     }
     if not args.no_cpu_baseline and args.workload in (1, 2, 3):
         res["cpu_baseline"] = cpu_baseline(wl, step_bytes, args.cpu_seconds)
