@@ -27,6 +27,9 @@ from .reference import (  # noqa: F401
     verify_scores_grouped,
     topk_select,
     sparse_draft_attention,
+    verify_scores_per_head,
+    sparse_draft_attention_per_head,
+    sink_window_select,
     compact_kv,
     dense_draft_attention,
     build_best_first_tree,

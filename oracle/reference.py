@@ -32,6 +32,11 @@ Pins (tests/test_oracle_*.py):
                           argmax) on tiny inputs with exact ties; golden cases
   sparse_draft_attention -- idx = whole prefix == dense decode; permutation
                           invariance; golden 2-key case
+  verify_scores_per_head -- summed over the KV heads == verify_scores; one KV
+                          head == verify_scores
+  sparse_draft_attention_per_head -- the same list for every head ==
+                          sparse_draft_attention
+  sink_window_select   -- written out by hand on small cases
   build_best_first_tree -- brute force: node i is the i-th best of every node
                           reachable within the depth limit; golden tie order;
                           equal to the input generator's trees
@@ -270,6 +275,61 @@ def sparse_draft_attention(q1: np.ndarray, dtype: str, kv: KVCache,
             lg = scale * (Kg @ qf[b, hs].T)                        # [n][G]
             out[b, hs] = _softmax_attend(lg, Vg)
     return out
+
+
+# ----------------------------------------------------------------------------
+# selection variants: one key set per KV head (the score of Vegas §2.A summed
+# over the query heads of one group only), and a query-agnostic sink + recent
+# window (the selector the Vegas results section compares against)
+
+def verify_scores_per_head(q: np.ndarray, dtype: str, kv: KVCache, P: np.ndarray,
+                           score_rows: Sequence[int], scale: float, Hkv: int,
+                           P_max: Optional[int] = None) -> np.ndarray:
+    """s_{b,g,i} = sum_{t in score_rows} sum_{h in group g} scale * q_{b,t,h} . k_{b,i,g}, i < P_b.
+
+    Returns float64 [B][Hkv][P_max]; entries i >= P_b are NaN."""
+    qf = _f64(q, dtype)
+    B, N, Hq, D = qf.shape
+    G = Hq // Hkv
+    if P_max is None:
+        P_max = int(np.max(P)) if B else 0
+    s = np.full((B, Hkv, P_max), np.nan)
+    rows = [int(t) for t in score_rows]
+    for b in range(B):
+        Pb = int(P[b])
+        for g in range(Hkv):
+            Kg = kv.keys(b, g, np.arange(Pb))
+            acc = np.zeros(Pb)
+            for t in rows:
+                for h in range(g * G, (g + 1) * G):
+                    acc += scale * (Kg @ qf[b, t, h])
+            s[b, g, :Pb] = acc
+    return s
+
+
+def sparse_draft_attention_per_head(q1: np.ndarray, dtype: str, kv: KVCache,
+                                    idx: Sequence[Sequence[np.ndarray]], scale: float, Hkv: int) -> np.ndarray:
+    """One draft query per sequence; the query heads of KV group g attend to
+    exactly the keys idx[b][g].  Returns float64 [B][Hq][D]; an empty list gives 0."""
+    qf = _f64(q1, dtype)
+    B, Hq, D = qf.shape
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        for g in range(Hkv):
+            ib = np.asarray(idx[b][g], dtype=np.int64)
+            if ib.size == 0:
+                continue
+            hs = list(range(g * G, (g + 1) * G))
+            lg = scale * (kv.keys(b, g, ib) @ qf[b, hs].T)
+            out[b, hs] = _softmax_attend(lg, kv.values(b, g, ib))
+    return out
+
+
+def sink_window_select(P_b: int, sink: int, window: int) -> np.ndarray:
+    """The first `sink` and the last `window` prefix positions, increasing."""
+    keep = set(range(min(sink, P_b))) | set(range(max(0, P_b - window), P_b))
+    return np.asarray(sorted(keep), dtype=np.int64)
 
 
 # ----------------------------------------------------------------------------

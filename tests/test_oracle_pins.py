@@ -521,3 +521,43 @@ def test_best_first_tree_golden_ties_and_generator():
         o = oracle.build_best_first_tree(lpg, n, dmax)
         for a, b in zip(g, o):
             assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- selection variants
+
+def test_per_head_scores_sum_to_the_total():
+    wl = make_custom(seed=41, dtype="bf16", B=2, Hq=8, Hkv=2, D=64, P=[90, 57], N=4, score_rows="all")
+    kv = KVCache.of(wl)
+    ph = oracle.verify_scores_per_head(wl.q, "bf16", kv, wl.P, wl.score_rows, wl.scale, 2)
+    tot = oracle.verify_scores(wl.q, "bf16", kv, wl.P, wl.score_rows, wl.scale, 2)
+    np.testing.assert_allclose(ph.sum(axis=1), tot, rtol=1e-12, atol=1e-12, equal_nan=True)
+    # one KV head: the per-head score is the total
+    wl1 = make_custom(seed=42, dtype="f32", B=1, Hq=4, Hkv=1, D=64, P=70, N=3, score_rows=[0, 2])
+    kv1 = KVCache.of(wl1)
+    np.testing.assert_allclose(oracle.verify_scores_per_head(wl1.q, "f32", kv1, wl1.P, wl1.score_rows, wl1.scale, 1)[:, 0],
+                               oracle.verify_scores(wl1.q, "f32", kv1, wl1.P, wl1.score_rows, wl1.scale, 1),
+                               rtol=1e-12, atol=1e-12, equal_nan=True)
+
+
+def test_per_head_draft_with_shared_lists_is_the_shared_step():
+    wl = make_custom(seed=43, dtype="bf16", B=2, Hq=8, Hkv=2, D=64, P=[120, 80], N=2, q_std_mult=4.0)
+    kv = KVCache.of(wl)
+    rng = np.random.default_rng(2)
+    idx = [np.sort(rng.choice(int(wl.P[b]), 30, replace=False)) for b in range(2)]
+    a = oracle.sparse_draft_attention_per_head(wl.dq[0], "bf16", kv, [[i, i] for i in idx], wl.scale, 2)
+    b = oracle.sparse_draft_attention(wl.dq[0], "bf16", kv, idx, wl.scale, 2)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    # different lists per head: head group g sees only its own list
+    other = [np.sort(rng.choice(int(wl.P[b]), 12, replace=False)) for b in range(2)]
+    c = oracle.sparse_draft_attention_per_head(wl.dq[0], "bf16", kv, [[idx[b], other[b]] for b in range(2)],
+                                               wl.scale, 2)
+    d = oracle.sparse_draft_attention(wl.dq[0], "bf16", kv, other, wl.scale, 2)
+    np.testing.assert_allclose(c[:, :4], b[:, :4], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(c[:, 4:], d[:, 4:], rtol=1e-12, atol=1e-15)
+
+
+def test_sink_window_select_by_hand():
+    assert oracle.sink_window_select(10, 2, 3).tolist() == [0, 1, 7, 8, 9]
+    assert oracle.sink_window_select(4, 2, 3).tolist() == [0, 1, 2, 3]      # overlap
+    assert oracle.sink_window_select(0, 2, 3).tolist() == []
+    assert oracle.sink_window_select(100, 0, 5).tolist() == [95, 96, 97, 98, 99]
