@@ -16,6 +16,9 @@
  *   sv_compact_kv, sv_dense_draft_attn   the same draft steps over the set
  *                         gathered once into dense buffers, plus a tail of
  *                         drafted tokens' rows.
+ *   sv_verify_attn_per_head, sv_sparse_draft_attn_per_head, sv_select_sink_window
+ *                         selection variants: one key set per KV head, and a
+ *                         sink + recent-window baseline.
  *   sv_build_tree         best-first draft tree (parent array) from per-depth
  *                         draft log-probabilities.
  *   sv_accept_commit      greedy acceptance of the verified drafts and the
@@ -178,6 +181,39 @@ sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int
                                const sv_kv_cache* kv, const int32_t* idx, int idx_stride,
                                const int32_t* n_idx, int max_idx, float softmax_scale, void* out,
                                void* workspace, size_t workspace_bytes, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Selection variants.
+ *
+ * Per-KV-head selection: the score of Vegas §2.A kept per KV head g (summed
+ * over the scoring rows and the query heads of group g only), so each KV head
+ * can keep its own k entries; the draft step then reads one list per KV head.
+ *
+ * sv_verify_attn_per_head: exactly sv_verify_attn, except that head_scores
+ *   is fp32 [B][Hkv][P_max]: head_scores[b][g][i] = sum_{t in score_rows}
+ *   sum_{h in group g} scale * q[b][t][h] . k[b][i][g], entries i < P_b
+ *   written; summed over g it is sv_verify_attn's score.  Selection per head is
+ *   sv_topk_select over the B * Hkv rows (prefix_len and k given per row).
+ * sv_sparse_draft_attn_per_head: exactly sv_sparse_draft_attn, except that
+ *   idx is [B][Hkv][idx_stride] and n_idx [B][Hkv]: the query heads of group g
+ *   attend to the list of KV head g.
+ *
+ * sv_select_sink_window: the query-agnostic baseline the Vegas results
+ * compare against (attention sinks plus a recent window): idx[b] = the first
+ * `sink` and the last `window` prefix positions, increasing, then -1 up to
+ * k_max; count[b] (may be NULL) their number.  Needs k_max >= sink + window.
+ */
+sv_status sv_verify_attn_per_head(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                                  const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                                  const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,
+                                  float softmax_scale, void* out, float* head_scores,
+                                  void* workspace, size_t workspace_bytes, sv_stream stream);
+sv_status sv_sparse_draft_attn_per_head(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D,
+                                        const sv_kv_cache* kv, const int32_t* idx, int idx_stride,
+                                        const int32_t* n_idx, int max_idx, float softmax_scale, void* out,
+                                        void* workspace, size_t workspace_bytes, sv_stream stream);
+sv_status sv_select_sink_window(int B, int P_max, const int32_t* prefix_len, int sink, int window, int k_max,
+                                int32_t* idx, int32_t* count, sv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* Draft loop over a compacted KV.  The draft model's attention is called once

@@ -183,6 +183,23 @@ def test_build_tree_rejects_bad_arguments():
     assert bt(0, 16, 8, 32, None, None, None, None, None) == _lib.SV_OK
 
 
+def test_selection_variants_reject_bad_arguments():
+    lib = _lib.load()
+    sw = lib.sv_select_sink_window
+    assert sw(1, 100, FAKE, 4, 8, 11, FAKE, None, None) == _lib.SV_E_INVALID     # k_max < sink + window
+    assert sw(1, 100, FAKE, -1, 8, 11, FAKE, None, None) == _lib.SV_E_INVALID
+    assert sw(1, 100, None, 4, 8, 12, FAKE, None, None) == _lib.SV_E_INVALID
+    assert sw(0, 100, None, 4, 8, 12, None, None, None) == _lib.SV_OK
+    kv = _kv()
+    sp = lib.sv_sparse_draft_attn_per_head
+    assert sp(FAKE, _lib.SV_BF16, 1, 32, 8, 128, ctypes.byref(kv), FAKE, 10, FAKE, 20, 0.0, FAKE, FAKE, 1 << 30,
+              None) == _lib.SV_E_INVALID                       # max_idx > idx_stride
+    vp = lib.sv_verify_attn_per_head
+    rows = (ctypes.c_int32 * 2)(0, 7)
+    assert vp(FAKE, _lib.SV_BF16, 1, 8, 30, 8, 128, ctypes.byref(kv), FAKE, 100, None, rows, 2, 0.0, FAKE, FAKE,
+              FAKE, 1 << 30, None) == _lib.SV_E_INVALID          # Hq not a multiple of Hkv
+
+
 def test_timing_events_must_pair():
     lib = _lib.load()
     assert lib.sv_set_verify_timing_events(FAKE, None) == _lib.SV_E_INVALID

@@ -25,7 +25,8 @@ from ._lib import SvError, SV_F32, SV_BF16  # noqa: F401
 
 __all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn", "compact_kv",
            "dense_draft_attn", "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size",
-           "dense_draft_workspace_size", "build_tree", "accept_commit", "timing_events", "SvError", "lib"]
+           "dense_draft_workspace_size", "build_tree", "accept_commit", "verify_attn_per_head",
+           "sparse_draft_attn_per_head", "select_sink_window", "timing_events", "SvError", "lib"]
 
 
 def lib() -> ctypes.CDLL:
@@ -185,6 +186,60 @@ def sparse_draft_attn(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, n_idx: to
                                       _ptr(n_idx), max_idx, float(scale), _ptr(out), wptr, wlen,
                                       _stream(q.device)))
     return out
+
+
+def verify_attn_per_head(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max: int,
+                         parent: Optional[torch.Tensor] = None, score_rows: Sequence[int] = (0,),
+                         scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                         head_scores: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
+    """sv_verify_attn_per_head: -> (out [B][N][Hq][D], head_scores fp32 [B][Hkv][P_max])."""
+    L = lib()
+    B, N, Hq, D = (int(x) for x in q.shape)
+    rows = [int(r) for r in score_rows]
+    if out is None:
+        out = torch.empty_like(q)
+    if head_scores is None:
+        head_scores = torch.empty((B, kv.Hkv, P_max), dtype=torch.float32, device=q.device)
+    rows_arr = (ctypes.c_int32 * max(1, len(rows)))(*rows)
+    dt = _dtype_code(q)
+    nbytes = verify_workspace_size(B, N, Hq, kv.Hkv, D, P_max, dt, parent is not None, len(rows),
+                                   kv.page_size if kv.page_table is not None else 0)
+    wptr, wlen = _ws(workspace, "verify").get(nbytes, q.device)
+    kvs = kv.c_struct()
+    _lib.check(L.sv_verify_attn_per_head(_ptr(q), dt, B, N, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(prefix_len),
+                                         P_max, _ptr(parent), rows_arr, len(rows), float(scale), _ptr(out),
+                                         _ptr(head_scores), wptr, wlen, _stream(q.device)))
+    return out, head_scores
+
+
+def sparse_draft_attn_per_head(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, n_idx: torch.Tensor, *,
+                               max_idx: Optional[int] = None, scale: float = 0.0,
+                               out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
+    """sv_sparse_draft_attn_per_head: idx int32 [B][Hkv][stride], n_idx int32 [B][Hkv]."""
+    L = lib()
+    B, Hq, D = (int(x) for x in q.shape)
+    stride = int(idx.shape[2])
+    max_idx = stride if max_idx is None else int(max_idx)
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _dtype_code(q)
+    wptr, wlen = _ws(workspace, "sparse").get(sparse_workspace_size(B, Hq, kv.Hkv, D, max_idx), q.device)
+    kvs = kv.c_struct()
+    _lib.check(L.sv_sparse_draft_attn_per_head(_ptr(q), dt, B, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(idx), stride,
+                                               _ptr(n_idx), max_idx, float(scale), _ptr(out), wptr, wlen,
+                                               _stream(q.device)))
+    return out
+
+
+def select_sink_window(prefix_len: torch.Tensor, P_max: int, sink: int, window: int, k_max: int):
+    """sv_select_sink_window: -> (idx int32 [B][k_max], count int32 [B])."""
+    L = lib()
+    B = int(prefix_len.shape[0])
+    idx = torch.empty((B, k_max), dtype=torch.int32, device=prefix_len.device)
+    count = torch.empty((B,), dtype=torch.int32, device=prefix_len.device)
+    _lib.check(L.sv_select_sink_window(B, int(P_max), _ptr(prefix_len), int(sink), int(window), int(k_max), _ptr(idx),
+                                       _ptr(count), _stream(prefix_len.device)))
+    return idx, count
 
 
 def compact_kv(kv: KVCache, idx: torch.Tensor, n_idx: torch.Tensor, cap: int, *, max_idx: Optional[int] = None,

@@ -16,6 +16,7 @@ EXPORTS = (
     "sv_verify_workspace_size", "sv_verify_attn",
     "sv_topk_workspace_size", "sv_topk_select",
     "sv_sparse_workspace_size", "sv_sparse_draft_attn",
+    "sv_verify_attn_per_head", "sv_sparse_draft_attn_per_head", "sv_select_sink_window",
     "sv_compact_kv", "sv_dense_draft_workspace_size", "sv_dense_draft_attn", "sv_build_tree",
     "sv_accept_commit",
     "sv_set_verify_timing_events",
@@ -72,6 +73,12 @@ def load() -> ctypes.CDLL:
     lib.sv_sparse_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.sv_sparse_draft_attn.restype = i32
     lib.sv_sparse_draft_attn.argtypes = [vp, i32, i32, i32, i32, i32, kvp, vp, i32, vp, i32, f32, vp, vp, sz, vp]
+    lib.sv_verify_attn_per_head.restype = i32
+    lib.sv_verify_attn_per_head.argtypes = lib.sv_verify_attn.argtypes
+    lib.sv_sparse_draft_attn_per_head.restype = i32
+    lib.sv_sparse_draft_attn_per_head.argtypes = lib.sv_sparse_draft_attn.argtypes
+    lib.sv_select_sink_window.restype = i32
+    lib.sv_select_sink_window.argtypes = [i32, i32, vp, i32, i32, i32, vp, vp, vp]
     lib.sv_compact_kv.restype = i32
     lib.sv_compact_kv.argtypes = [i32, i32, i32, i32, kvp, vp, i32, vp, i32, vp, vp, i32, vp]
     lib.sv_dense_draft_workspace_size.restype = sz

@@ -93,11 +93,14 @@ size_t sv_verify_workspace_size(int B, int N, int Hq, int Hkv, int D, int P_max,
   return sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, is_tree != 0, n_score_rows, page_size).bytes;
 }
 
-sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
-                         const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
-                         const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,
-                         float softmax_scale, void* out, float* scores, void* workspace,
-                         size_t workspace_bytes, sv_stream stream) {
+}  // extern "C"
+
+namespace {
+
+sv_status verify_common(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D, const sv_kv_cache* kv,
+                        const int32_t* prefix_len, int P_max, const int32_t* parent, const int32_t* score_rows_host,
+                        int n_score_rows, float softmax_scale, void* out, float* scores, void* workspace,
+                        size_t workspace_bytes, sv_stream stream, int head_scores) {
   sv_status st;
   if ((st = check_dtype(dtype))) return st;
   if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
@@ -127,8 +130,30 @@ sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, in
     return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
   const int e = sv::launch_verify(p, q, kv_args(kv), prefix_len, parent, score_rows_host, n_score_rows,
                                   resolve_scale(softmax_scale, D), out, scores, workspace, stream, g_ev_start,
-                                  g_ev_stop);
+                                  g_ev_stop, 0, head_scores);
   return hip_status(e, "sv_verify_attn launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                         const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                         const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,
+                         float softmax_scale, void* out, float* scores, void* workspace,
+                         size_t workspace_bytes, sv_stream stream) {
+  return verify_common(q, dtype, B, N, Hq, Hkv, D, kv, prefix_len, P_max, parent, score_rows_host, n_score_rows,
+                       softmax_scale, out, scores, workspace, workspace_bytes, stream, 0);
+}
+
+sv_status sv_verify_attn_per_head(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                                  const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                                  const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,
+                                  float softmax_scale, void* out, float* head_scores, void* workspace,
+                                  size_t workspace_bytes, sv_stream stream) {
+  return verify_common(q, dtype, B, N, Hq, Hkv, D, kv, prefix_len, P_max, parent, score_rows_host, n_score_rows,
+                       softmax_scale, out, head_scores, workspace, workspace_bytes, stream, 1);
 }
 
 size_t sv_topk_workspace_size(int B, int P_max) {
@@ -155,10 +180,13 @@ size_t sv_sparse_workspace_size(int B, int Hq, int Hkv, int D, int max_idx) {
   return sv::plan_sparse(B, Hq, Hkv, D, max_idx).bytes;
 }
 
-sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D,
-                               const sv_kv_cache* kv, const int32_t* idx, int idx_stride, const int32_t* n_idx,
-                               int max_idx, float softmax_scale, void* out, void* workspace,
-                               size_t workspace_bytes, sv_stream stream) {
+}  // extern "C"
+
+namespace {
+
+sv_status sparse_common(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D, const sv_kv_cache* kv,
+                        const int32_t* idx, int idx_stride, const int32_t* n_idx, int max_idx, float softmax_scale,
+                        void* out, void* workspace, size_t workspace_bytes, sv_stream stream, int per_head) {
   sv_status st;
   if ((st = check_dtype(dtype))) return st;
   if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
@@ -173,8 +201,40 @@ sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int
   if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
     return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
   return hip_status(sv::launch_sparse(p, (int)dtype, q, kv_args(kv), idx, idx_stride, n_idx,
-                                      resolve_scale(softmax_scale, D), out, workspace, stream),
+                                      resolve_scale(softmax_scale, D), out, workspace, stream, per_head),
                     "sv_sparse_draft_attn launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status sv_sparse_draft_attn(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D,
+                               const sv_kv_cache* kv, const int32_t* idx, int idx_stride, const int32_t* n_idx,
+                               int max_idx, float softmax_scale, void* out, void* workspace,
+                               size_t workspace_bytes, sv_stream stream) {
+  return sparse_common(q, dtype, B, Hq, Hkv, D, kv, idx, idx_stride, n_idx, max_idx, softmax_scale, out, workspace,
+                       workspace_bytes, stream, 0);
+}
+
+sv_status sv_sparse_draft_attn_per_head(const void* q, sv_dtype dtype, int B, int Hq, int Hkv, int D,
+                                        const sv_kv_cache* kv, const int32_t* idx, int idx_stride,
+                                        const int32_t* n_idx, int max_idx, float softmax_scale, void* out,
+                                        void* workspace, size_t workspace_bytes, sv_stream stream) {
+  return sparse_common(q, dtype, B, Hq, Hkv, D, kv, idx, idx_stride, n_idx, max_idx, softmax_scale, out, workspace,
+                       workspace_bytes, stream, 1);
+}
+
+sv_status sv_select_sink_window(int B, int P_max, const int32_t* prefix_len, int sink, int window, int k_max,
+                                int32_t* idx, int32_t* count, sv_stream stream) {
+  if (B < 0 || P_max < 0) return fail(SV_E_INVALID, "B and P_max must be >= 0");
+  if (sink < 0 || window < 0) return fail(SV_E_INVALID, "sink and window must be >= 0");
+  if (k_max < sink + window) return fail(SV_E_INVALID, "k_max = %d is smaller than sink + window = %d", k_max,
+                                         sink + window);
+  if (B == 0) return ok();
+  if (!prefix_len || (!idx && k_max > 0)) return fail(SV_E_INVALID, "prefix_len and idx must be non-NULL");
+  return hip_status(sv::launch_sink_window(B, P_max, prefix_len, sink, window, k_max, idx, count, stream),
+                    "sv_select_sink_window launch");
 }
 
 sv_status sv_compact_kv(sv_dtype dtype, int B, int Hkv, int D, const sv_kv_cache* kv, const int32_t* idx,

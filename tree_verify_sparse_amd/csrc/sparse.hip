@@ -26,6 +26,7 @@ struct SparseArgs {
   float* ws_o;
   f32x2* ws_ml;
   int B, Hq, Hkv, G, idx_stride, max_idx, n_chunks;
+  int per_head;  // 1: one index list per (sequence, KV head)
   float scale_log2;
 };
 
@@ -43,7 +44,8 @@ __global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
   __shared__ float mls[kMaxG][2];
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  int n = a.n_idx[b];
+  const long long lst = a.per_head ? (long long)b * a.Hkv + g : b;  // this KV head's list
+  int n = a.n_idx[lst];
   n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
   const int k0 = c * kChunk;
   if (k0 >= n) return;
@@ -59,7 +61,7 @@ __global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
   for (int i = 0; i < LOADS; ++i) {
     const int e = tid + 256 * i, key = e / CPR, col = e % CPR;
     long long s = -1;
-    if (key < nk) s = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + k0 + key]);
+    if (key < nk) s = a.kv.slot(b, a.idx[lst * a.idx_stride + k0 + key]);
     if (s < 0) s = 0;  // unused or unmapped entries read slot 0 and are masked below
     kx[i] = *reinterpret_cast<const uint4*>(kb + s * sb + col * 16);
     vx[i] = *reinterpret_cast<const uint4*>(vb + s * sb + col * 16);
@@ -132,7 +134,7 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   const int bh = blockIdx.x * 4 + wave;
   if (bh >= a.B * a.Hq) return;
   const int b = bh / a.Hq;
-  int n = a.n_idx[b];
+  int n = a.n_idx[a.per_head ? (long long)b * a.Hkv + (bh % a.Hq) / a.G : b];
   n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
   const int nc = (n + kChunk - 1) / kChunk;
   const long long rec0 = (long long)bh * a.n_chunks;
@@ -249,6 +251,31 @@ int launch_compact(int dtype, int B, int Hkv, int D, const KvArgs& kv, const int
   return (int)hipGetLastError();
 }
 
+// Query-agnostic baseline selection: the first `sink` and the last `window`
+// prefix positions, in increasing order, then -1 up to k_max (the same
+// output format as the top-k selection).
+__global__ void __launch_bounds__(256) sink_window(const int32_t* prefix_len, int P_max, int sink, int window,
+                                                   int k_max, int32_t* idx, int32_t* count) {
+  const int b = blockIdx.x;
+  int P = prefix_len[b];
+  P = P < 0 ? 0 : (P > P_max ? P_max : P);
+  const int s = min(sink, P);
+  const int w0 = max(s, P - window);
+  const int n = s + (P - w0);
+  for (int j = threadIdx.x; j < k_max; j += 256)
+    idx[(long long)b * k_max + j] = j < s ? j : (j < n ? w0 + (j - s) : -1);
+  if (threadIdx.x == 0 && count) count[b] = n;
+}
+
+int launch_sink_window(int B, int P_max, const int32_t* prefix_len, int sink, int window, int k_max, int32_t* idx,
+                       int32_t* count, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (B == 0) return 0;
+  hipLaunchKernelGGL(sink_window, dim3(B), dim3(256), 0, st, prefix_len, P_max, sink, window, k_max, idx, count);
+  return (int)hipGetLastError();
+}
+
 SparsePlan plan_sparse(int B, int Hq, int Hkv, int D, int max_idx) {
   SparsePlan p{};
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.D = D; p.max_idx = max_idx;
@@ -270,7 +297,8 @@ static void launch_sparse_typed(const SparsePlan& p, const SparseArgs& a, hipStr
 }
 
 int launch_sparse(const SparsePlan& p, int dtype, const void* q, const KvArgs& kv, const int32_t* idx,
-                  int idx_stride, const int32_t* n_idx, float scale, void* out, void* ws, void* stream) {
+                  int idx_stride, const int32_t* n_idx, float scale, void* out, void* ws, void* stream,
+                  int per_head) {
   SparseArgs a{};
   a.q = q;
   a.out = out;
@@ -282,6 +310,7 @@ int launch_sparse(const SparsePlan& p, int dtype, const void* q, const KvArgs& k
   a.ws_ml = reinterpret_cast<f32x2*>(w + p.off_ml);
   a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.idx_stride = idx_stride; a.max_idx = p.max_idx;
   a.n_chunks = p.n_chunks;
+  a.per_head = per_head;
   a.scale_log2 = scale * kLog2e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();

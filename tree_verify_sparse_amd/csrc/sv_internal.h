@@ -57,7 +57,7 @@ struct KvArgs {
 int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const int32_t* prefix_len,
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
                   void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
-                  int len_bias = 0);
+                  int len_bias = 0, int head_scores = 0);
 // Best-first draft trees from per-depth log-probabilities (one wave per sequence).
 int launch_build_tree(int B, int n, int max_depth, int n_cand, const double* lp, int32_t* parent, int32_t* depth,
                       int32_t* rank, void* stream);
@@ -72,7 +72,12 @@ int launch_topk(const float* scores, int B, int P_max, const int32_t* prefix_len
                 int k_max, int32_t* idx, int32_t* count, void* ws, void* stream);
 size_t topk_workspace_bytes(int B, int P_max);
 bool topk_supported(int P_max);
+// per_head: idx is [B][Hkv][idx_stride] and n_idx [B][Hkv], one list per KV head.
 int launch_sparse(const SparsePlan& p, int dtype, const void* q, const KvArgs& kv, const int32_t* idx,
-                  int idx_stride, const int32_t* n_idx, float scale, void* out, void* ws, void* stream);
+                  int idx_stride, const int32_t* n_idx, float scale, void* out, void* ws, void* stream,
+                  int per_head = 0);
+// The first `sink` and the last `window` prefix positions of each sequence.
+int launch_sink_window(int B, int P_max, const int32_t* prefix_len, int sink, int window, int k_max, int32_t* idx,
+                       int32_t* count, void* stream);
 
 }  // namespace sv

@@ -95,6 +95,7 @@ struct VerifyArgs {
   float scale, scale_log2;
   int n_score_rows;
   int len_bias;  // 0 for verification; -1 for a decode over rows [0, prefix_len[b]) (see seq_prefix)
+  int head_scores;  // 1: scores are per KV head, [B][Hkv][P_max] (no sum over the groups)
   uint16_t score_rows[kMaxNodes];
 };
 
@@ -1493,6 +1494,11 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
     int Pb = a.prefix_len[b];
     Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
     if (i >= Pb) return;
+    if (a.head_scores) {  // each KV head's own sum over its query heads and the scoring rows
+      for (int g = 0; g < a.Hkv; ++g)
+        a.scores[((long long)b * a.Hkv + g) * a.P_max + i] = a.ws_s[((long long)b * a.Hkv + g) * a.s_stride + i];
+      return;
+    }
     float s = 0.f;
 #pragma unroll 8
     for (int g = 0; g < a.Hkv; ++g) s += a.ws_s[((long long)b * a.Hkv + g) * a.s_stride + i];
@@ -1736,7 +1742,7 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
 int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const int32_t* prefix_len,
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
                   void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
-                  int len_bias) {
+                  int len_bias, int head_scores) {
   VerifyArgs a{};
   a.q = q;
   a.out = out;
@@ -1765,6 +1771,7 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
   a.scale_log2 = scale * kLog2e;
   a.n_score_rows = n_score_rows;
   a.len_bias = len_bias;
+  a.head_scores = head_scores;
   for (int i = 0; i < n_score_rows && i < kMaxNodes; ++i) a.score_rows[i] = (uint16_t)score_rows[i];
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
