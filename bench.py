@@ -53,6 +53,10 @@ def parse():
                     help="draft steps gather the selected rows each time (sparse), or the set is gathered "
                          "once into dense buffers and every step streams them (compact); auto: compact "
                          "when the workload has more than one draft step")
+    ap.add_argument("--selection", choices=["scores", "per_head", "sink_window"], default="scores",
+                    help="scores: one key set per sequence from the fused scores (the method); per_head: one "
+                         "set per KV head from per-head scores; sink_window: the first 64 and the last k - 64 "
+                         "positions, no scores (the query-agnostic baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
@@ -152,6 +156,30 @@ def main():
         ddargs = [(dqs[s].data_ptr(), dt, wl.B, wl.Hq, wl.Hkv, wl.D, ck.data_ptr(), cv.data_ptr(), max(1, kmax),
                    count.data_ptr(), 0.0, douts[s].data_ptr(), dws.data_ptr(), dws_n, sp) for s in range(n_draft)]
     f_compact, f_dense = L.sv_compact_kv, L.sv_dense_draft_attn
+    # selection variants (the method's fused scores by default)
+    selection = args.selection
+    if selection == "per_head":
+        H = wl.Hkv
+        hscores = torch.empty((wl.B, H, wl.P_max), dtype=torch.float32, device=dev)
+        P_rows = i32(np.repeat(wl.P, H))
+        k_rows = i32(np.repeat(wl.k_sel, H))
+        hidx = torch.empty((wl.B, H, kmax), dtype=torch.int32, device=dev)
+        hcount = torch.empty((wl.B, H), dtype=torch.int32, device=dev)
+        tws_h = torch.empty(max(1, sv.topk_workspace_size(wl.B * H, wl.P_max)), dtype=torch.uint8, device=dev)
+        vargs = [a[:15] + (hscores.data_ptr(),) + a[16:] for a in vargs]
+        targs = (hscores.data_ptr(), wl.B * H, wl.P_max, P_rows.data_ptr(), k_rows.data_ptr(), kmax,
+                 hidx.data_ptr(), hcount.data_ptr(), tws_h.data_ptr(), tws_h.numel(), sp)
+        dargs = [[(dqs[s].data_ptr(), dt, wl.B, wl.Hq, wl.Hkv, wl.D, ctypes.byref(kv), hidx.data_ptr(), kmax,
+                   hcount.data_ptr(), kmax, 0.0, douts[s].data_ptr(), sws.data_ptr(), sws_n, sp)
+                  for s in range(n_draft)] for kv in kvs]
+        f_verify, f_sparse = L.sv_verify_attn_per_head, L.sv_sparse_draft_attn_per_head
+        draft_path = "sparse"  # one list per KV head: the per-head gathered step
+    elif selection == "sink_window":
+        sink = min(64, kmax)
+        window = kmax - sink
+        vargs = [a[:11] + (rows_arr, 0) + a[13:15] + (None,) + a[16:] for a in vargs]  # no scores
+        targs = (wl.B, wl.P_max, P.data_ptr(), sink, window, kmax, idx.data_ptr(), count.data_ptr(), sp)
+        f_topk = L.sv_select_sink_window
 
     def step(i, ev=None):
         c = i % copies
@@ -312,7 +340,8 @@ def main():
         "config": {"workload": CONFIG_NAMES[args.workload], "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D,
                    "prefix": int(wl.P_max) if wl.B == 1 else [int(x) for x in wl.P], "verify_nodes": wl.N,
                    "tree": wl.parent is not None, "score_rows": len(rows), "k": int(wl.k_sel.max()),
-                   "draft_steps": n_draft, "draft_path": draft_path, "paged": wl.layout == "paged",
+                   "draft_steps": n_draft, "draft_path": draft_path, "selection": selection,
+                   "paged": wl.layout == "paged",
                    "kv_copies_rotated": copies,
                    "step_bytes": step_bytes, "parallelism": "single-gpu"},
         "roofline": roof,

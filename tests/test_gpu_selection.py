@@ -38,7 +38,9 @@ def test_per_head_scores_selection_and_draft(name):
     wl = CASES[name]()
     dw = DevWorkload(wl)
     rows = [int(r) for r in wl.score_rows]
-    out, hs = sv.verify_attn_per_head(dw.q, dw.kv, dw.P, P_max=wl.P_max, parent=dw.parent, score_rows=rows)
+    hs0 = torch.zeros((wl.B, wl.Hkv, wl.P_max), dtype=torch.float32, device="cuda")  # entries past P_b stay 0
+    out, hs = sv.verify_attn_per_head(dw.q, dw.kv, dw.P, P_max=wl.P_max, parent=dw.parent, score_rows=rows,
+                                      head_scores=hs0)
     kv = OKV.of(wl)
     ref = oracle.verify_scores_per_head(wl.q, wl.dtype, kv, wl.P, rows, wl.scale, wl.Hkv, wl.P_max)
     g = as_f64(hs)
