@@ -3,19 +3,24 @@
 // whose pages hold a single token, with token indices used as page indices).
 //
 // One 256-thread workgroup per (sequence, KV head, chunk of kChunk listed
-// positions): it gathers the chunk's K and V rows of that head (each a
-// contiguous D-element row, so every gather is whole 128-byte lines) into LDS,
-// forms the logits of the G query heads sharing the KV head, and writes a
-// partial (m, l, o) per query head.  A second kernel merges the chunks with
-// log-sum-exp weights.  The work is a few FLOP per byte, so it runs on the
-// vector ALUs; the gathers are what costs.
+// positions).  Each wave gathers 16 of the chunk's K and V rows of that head
+// straight into registers: a row is CPR = row bytes / 16 consecutive lanes (a
+// lane group), each holding one 16-byte piece, so every gather is whole
+// 128-byte lines.  The logits of the query heads sharing the KV head are
+// per-lane partial dot products summed over the group's lanes (DPP); each
+// lane group then forms its own (m, l, o) over its rows, and the groups'
+// partials are combined through LDS into one per query head and chunk.  A
+// second kernel merges the chunks with log-sum-exp weights.  The work is a
+// few FLOP per byte, so it runs on the vector ALUs; the gathers are what
+// costs.
 #include "sv_device.h"
 #include "sv_internal.h"
 
 namespace sv {
 
-constexpr int kChunk = 64;
-constexpr int kMaxG = 16;
+constexpr int kChunk = 64;     // listed positions per workgroup (16 per wave)
+constexpr int kMaxG = 16;      // query heads per KV head
+constexpr int kHeadGroup = 4;  // query heads per pass over the gathered rows
 
 struct SparseArgs {
   const void* q;
@@ -30,104 +35,176 @@ struct SparseArgs {
   float scale_log2;
 };
 
+// Sum over each aligned segment of W lanes, every lane getting its segment's
+// sum: DPP quad permutations and row mirrors inside a row of 16 lanes (no LDS
+// round trip), a lane shuffle across rows.
+template <int W>
+__device__ __forceinline__ float seg_sum(float x) {
+  if constexpr (W >= 2) x += dpp_f<0xB1, 0xf>(0.f, x);   // quad_perm [1, 0, 3, 2]
+  if constexpr (W >= 4) x += dpp_f<0x4E, 0xf>(0.f, x);   // quad_perm [2, 3, 0, 1]
+  if constexpr (W >= 8) x += dpp_f<0x141, 0xf>(0.f, x);  // row_half_mirror: the other quad of the 8
+  if constexpr (W >= 16) x += dpp_f<0x140, 0xf>(0.f, x); // row_mirror: the other 8 of the row
+  if constexpr (W >= 32) x += __shfl_xor(x, 16);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// The EPC elements of a 16-byte piece as floats.
+template <typename T, int EPC>
+__device__ __forceinline__ void piece_f(const uint4& raw, float (&x)[EPC]) {
+  const T* t = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+  for (int u = 0; u < EPC; ++u) x[u] = (float)t[u];
+}
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
   constexpr int ROWB = D * (int)sizeof(T);
-  constexpr int CPR = ROWB / 16;              // 16-byte pieces per row
-  constexpr int LOADS = kChunk * CPR / 256;   // pieces per thread per tensor
-  constexpr int EPC = 16 / (int)sizeof(T);    // elements per piece
-  constexpr int KSTR = D + EPC;               // LDS row stride (elements): +16 bytes spreads banks
-  __shared__ __attribute__((aligned(16))) T Ks[kChunk][KSTR];
-  __shared__ __attribute__((aligned(16))) T Vs[kChunk][D];
-  __shared__ __attribute__((aligned(16))) float qs[kMaxG][D];
-  __shared__ float lg[kMaxG][kChunk];
-  __shared__ float mls[kMaxG][2];
+  constexpr int CPR = ROWB / 16;   // lanes per gathered row (one 16-byte piece each)
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int RPW = 64 / CPR;    // rows a wave holds at once (lane groups)
+  constexpr int KW = kChunk / 4;   // listed positions per wave
+  constexpr int U = KW / RPW;      // positions per lane group
+  constexpr int HG = kHeadGroup;
+  static_assert(CPR <= 64 && RPW * U == KW && U >= 1, "gather geometry");
+  // one (m, l, o) partial per (wave, lane group, head of the group)
+  __shared__ __attribute__((aligned(16))) float red_o[4][RPW][HG][D];
+  __shared__ f32x2 red_ml[4][RPW][HG];
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane % CPR, r = lane / CPR;
   const long long lst = a.per_head ? (long long)b * a.Hkv + g : b;  // this KV head's list
-  int n = a.n_idx[lst];
-  n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
   const int k0 = c * kChunk;
+  int n = a.n_idx[lst];
+  // positions of this lane group's rows: their loads do not wait for the count
+  // (the list holds max_idx entries)
+  const int32_t* il = a.idx + lst * a.idx_stride + k0;
+  int pos[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int key = wave * KW + r + RPW * i;
+    pos[i] = k0 + key < a.max_idx ? il[key] : 0;
+  }
+  n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
   if (k0 >= n) return;
   const int nk = min(kChunk, n - k0);
   const int G = a.G;
 
-  // gather: every load of the chunk is issued before any is used
-  const char* kb = reinterpret_cast<const char*>(a.kv.k) + (long long)g * ROWB;
-  const char* vb = reinterpret_cast<const char*>(a.kv.v) + (long long)g * ROWB;
+  // gather: every load issued before any is used
+  const char* kb = reinterpret_cast<const char*>(a.kv.k) + (long long)g * ROWB + col * 16;
+  const char* vb = reinterpret_cast<const char*>(a.kv.v) + (long long)g * ROWB + col * 16;
   const long long sb = (long long)a.Hkv * ROWB;
-  uint4 kx[LOADS], vx[LOADS];
+  uint4 kx[U], vx[U];
+  bool ok[U];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int e = tid + 256 * i, key = e / CPR, col = e % CPR;
-    long long s = -1;
-    if (key < nk) s = a.kv.slot(b, a.idx[lst * a.idx_stride + k0 + key]);
-    if (s < 0) s = 0;  // unused or unmapped entries read slot 0 and are masked below
-    kx[i] = *reinterpret_cast<const uint4*>(kb + s * sb + col * 16);
-    vx[i] = *reinterpret_cast<const uint4*>(vb + s * sb + col * 16);
+  for (int i = 0; i < U; ++i) {
+    ok[i] = wave * KW + r + RPW * i < nk;
+    long long s = ok[i] ? a.kv.slot(b, pos[i]) : -1;
+    if (s < 0) s = 0;  // rows past the count read slot 0 and are masked below
+    kx[i] = *reinterpret_cast<const uint4*>(kb + s * sb);
+    vx[i] = *reinterpret_cast<const uint4*>(vb + s * sb);
   }
-  for (int e = tid; e < G * D; e += 256) {
-    const int j = e / D, d = e % D;
-    qs[j][d] = (float)reinterpret_cast<const T*>(a.q)[((long long)b * a.Hq + g * G + j) * D + d];
-  }
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int e = tid + 256 * i, key = e / CPR, col = e % CPR;
-    *reinterpret_cast<uint4*>(&Ks[key][col * EPC]) = kx[i];
-    *reinterpret_cast<uint4*>(&Vs[key][col * EPC]) = vx[i];
-  }
-  __syncthreads();
 
-  // logits: one (head, key) pair per thread, 16-byte LDS reads
-  for (int e = tid; e < G * kChunk; e += 256) {
-    const int j = e / kChunk, key = e % kChunk;
-    float acc = 0.f;
+  for (int j0 = 0; j0 < G; j0 += HG) {
+    // this lane's columns of the group's queries
+    float qf[HG][EPC];
 #pragma unroll
-    for (int cc = 0; cc < CPR; ++cc) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(&Ks[key][cc * EPC]);
-      const T* kt = reinterpret_cast<const T*>(&raw);
+    for (int jj = 0; jj < HG; ++jj) {
+      if (j0 + jj < G) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
+                                                          (((long long)b * a.Hq + g * G + j0 + jj) * D) * sizeof(T) +
+                                                          col * 16);
+        piece_f<T, EPC>(raw, qf[jj]);
+      } else {
 #pragma unroll
-      for (int u = 0; u < EPC; ++u) acc += qs[j][cc * EPC + u] * (float)kt[u];
+        for (int u = 0; u < EPC; ++u) qf[jj][u] = 0.f;
+      }
     }
-    lg[j][key] = key < nk ? acc * a.scale_log2 : kNegInf;
-  }
-  __syncthreads();
+    // logits (log2 domain): partial dot products summed over the lane group
+    float lg[U][HG];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float kf[EPC];
+      piece_f<T, EPC>(kx[i], kf);
+#pragma unroll
+      for (int jj = 0; jj < HG; ++jj) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < EPC; ++u) acc += qf[jj][u] * kf[u];
+        lg[i][jj] = seg_sum<CPR>(acc) * a.scale_log2;
+      }
+    }
+    // the lane group's partial over its U rows: every lane of the group holds
+    // the same logits, so m and l need no exchange; each lane sums P V for its
+    // own columns
+    float o[HG][EPC];
+#pragma unroll
+    for (int jj = 0; jj < HG; ++jj) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < U; ++i) mx = ok[i] ? fmaxf(mx, lg[i][jj]) : mx;
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const float p = (ok[i] && mx != kNegInf) ? fast_exp2(lg[i][jj] - mx) : 0.f;
+        lg[i][jj] = p;
+        ls += p;
+      }
+      if (col == 0) red_ml[wave][r][jj] = f32x2{mx, ls};
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) o[jj][u] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float vf[EPC];
+      piece_f<T, EPC>(vx[i], vf);
+#pragma unroll
+      for (int jj = 0; jj < HG; ++jj)
+#pragma unroll
+        for (int u = 0; u < EPC; ++u) o[jj][u] += lg[i][jj] * vf[u];
+    }
+#pragma unroll
+    for (int jj = 0; jj < HG; ++jj)
+#pragma unroll
+      for (int u = 0; u < EPC; u += 4)
+        *reinterpret_cast<f32x4*>(&red_o[wave][r][jj][col * EPC + u]) =
+            f32x4{o[jj][u], o[jj][u + 1], o[jj][u + 2], o[jj][u + 3]};
+    __syncthreads();
 
-  // softmax statistics per head: one wave per head, one lane per key
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int j = wave; j < G; j += 4) {
-    const float x = lg[j][lane];
-    const float mx = wave_max(x);
-    const float p = x == kNegInf ? 0.f : fast_exp2(x - mx);
-    const float ls = wave_sum(p);
-    lg[j][lane] = p;
-    if (lane == 0) {
-      mls[j][0] = mx;
-      mls[j][1] = ls;
+    // the group's 4 * RPW partials of each (head, column pair), combined in a fixed order
+    const int hg = min(HG, G - j0);
+    for (int e = tid; e < hg * (D / 2); e += 256) {
+      const int jj = e / (D / 2), d = 2 * (e % (D / 2));
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) M = fmaxf(M, red_ml[w][q][jj][0]);
+      float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+          const f32x2 ml = red_ml[w][q][jj];
+          const float wt = ml[0] == kNegInf ? 0.f : fast_exp2(ml[0] - M);
+          const f32x2 ov = *reinterpret_cast<const f32x2*>(&red_o[w][q][jj][d]);
+          L += wt * ml[1];
+          o0 += wt * ov[0];
+          o1 += wt * ov[1];
+        }
+      const long long rec = ((long long)b * a.Hq + g * G + j0 + jj) * a.n_chunks + c;
+      *reinterpret_cast<f32x2*>(a.ws_o + rec * D + d) = f32x2{o0, o1};
+      if (d == 0) a.ws_ml[rec] = f32x2{M, L};
     }
-  }
-  __syncthreads();
-
-  // P V: one (head, column pair) per thread
-  for (int e = tid; e < G * (D / 2); e += 256) {
-    const int j = e / (D / 2), d = 2 * (e % (D / 2));
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll 8
-    for (int key = 0; key < nk; ++key) {
-      const float p = lg[j][key];
-      a0 += p * (float)Vs[key][d];
-      a1 += p * (float)Vs[key][d + 1];
-    }
-    const long long rec = ((long long)b * a.Hq + g * G + j) * a.n_chunks + c;
-    *reinterpret_cast<f32x2*>(a.ws_o + rec * D + d) = f32x2{a0, a1};
-    if (d == 0) a.ws_ml[rec] = f32x2{mls[j][0], mls[j][1]};
+    if (j0 + HG < G) __syncthreads();  // the next group rewrites the partials
   }
 }
 
 // Chunk merge: one wave per (sequence, query head).  The pair's partials are
-// contiguous ([chunk][D] floats), so the wave fetches up to 256 / (D / 4)
-// chunks per round with one 16-byte load per lane per step, every load issued
-// before any is used; lanes holding the same columns are then summed.
+// contiguous ([chunk][D] floats); each lane keeps its own running (m, l, o)
+// over the chunks it reads, fetching a batch's (m, l) and o together (one
+// trip to memory per batch), and the lanes holding the same columns are
+// combined with log-sum-exp weights at the end.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -138,36 +215,46 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
   const int nc = (n + kChunk - 1) / kChunk;
   const long long rec0 = (long long)bh * a.n_chunks;
-  float M = kNegInf;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, a.ws_ml[rec0 + c][0]);
-  M = wave_max(M);
   constexpr int Q4 = D / 4;          // float4 column groups per row
   constexpr int CPL = 64 / Q4;       // chunks covered by one wave-wide load step
-  constexpr int STEPS = 8;           // load steps in flight per round
+  constexpr int STEPS = 16;          // load steps in flight per batch
   const int quad = lane % Q4, sub = lane / Q4;
+  float m = kNegInf, lsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
   for (int cb = 0; cb < nc; cb += CPL * STEPS) {
     f32x4 x[STEPS];
-    float w[STEPS];
+    f32x2 ml[STEPS];
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) {
       const int c = cb + j * CPL + sub;
       x[j] = c < nc ? *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * quad) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const f32x2 ml = c < nc ? a.ws_ml[rec0 + c] : f32x2{kNegInf, 0.f};
-      w[j] = (M == kNegInf || c >= nc) ? 0.f : fast_exp2(ml[0] - M);
-      if (quad == 0) lsum += w[j] * ml[1];
+      ml[j] = c < nc ? a.ws_ml[rec0 + c] : f32x2{kNegInf, 0.f};
     }
+    float bm = m;
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) acc += w[j] * x[j];
+    for (int j = 0; j < STEPS; ++j) bm = fmaxf(bm, ml[j][0]);
+    const float wa = m == kNegInf ? 0.f : fast_exp2(m - bm);
+    acc *= wa;
+    lsum *= wa;
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+      const float w = ml[j][0] == kNegInf ? 0.f : fast_exp2(ml[j][0] - bm);
+      acc += w * x[j];
+      lsum += w * ml[j][1];
+    }
+    m = bm;
   }
-  // lanes with the same quad (different sub) hold different chunks: sum them
+  // lanes with the same quad (different sub) hold different chunks
+  const float M = wave_max(m);
+  const float wl = m == kNegInf ? 0.f : fast_exp2(m - M);
+  acc *= wl;
+  lsum *= wl;
 #pragma unroll
   for (int o = Q4; o < 64; o <<= 1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], o);
+    lsum += __shfl_xor(lsum, o);
   }
-  lsum = wave_sum(lsum);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   if (sub == 0) {
     T* dst = reinterpret_cast<T*>(a.out) + (long long)bh * D + 4 * quad;
