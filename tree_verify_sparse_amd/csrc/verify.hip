@@ -1430,9 +1430,14 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
     const int gr = (int)blockIdx.x * (4 / wpr) + wave / wpr;  // (b, g, row); uniform over a row's waves
     if (gr >= a.B * a.Hkv * a.R) return;
     const int row = gr % a.R, bg = gr / a.R, g = bg % a.Hkv, b = bg / a.Hkv;
-    int L;
-    seq_prefix(a, b, &L);
-    const int nc = a.all_chunks ? a.n_chunks : min((L + a.chunk - 1) / a.chunk, a.n_chunks);
+    // every chunk holds a partial (streaming kernel), else the chunks below P_b + N;
+    // the branch keeps the sequence-length load off the first path
+    int nc = a.n_chunks;
+    if (!a.all_chunks) {
+      int L;
+      seq_prefix(a, b, &L);
+      nc = min((L + a.chunk - 1) / a.chunk, a.n_chunks);
+    }
     const long long rec0 = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks;
     static_assert(D / 4 <= 32, "one float4 column group per lane of a half");
     const int half = lane >> 5, q = lane & 31;
@@ -1512,23 +1517,36 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256) verify_prep(const VerifyArgs a, int n_qbar_wgs) {
   const int tid = threadIdx.x;
   __shared__ float part[256];
-  __shared__ uint32_t ancs[2][kMaxNodes][kAncWords];
-  __shared__ int jmp[2][kMaxNodes];
+  __shared__ __attribute__((aligned(16))) uint32_t ancs[kMaxNodes][kAncWords];
+  __shared__ int jmp[kMaxNodes];
   if ((int)blockIdx.x < n_qbar_wgs) {
     // partial qbar of (b, g) over pairs [sp * kQbarPairs, (sp + 1) * kQbarPairs):
-    // D columns x (256 / D) pair phases, loads unrolled so they are in flight together
+    // D columns x (256 / D) pair phases; every load of the thread is issued
+    // before the first is used (one trip to memory)
     const int sp = blockIdx.x % a.qsplit, bg = blockIdx.x / a.qsplit;
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     constexpr int NP = 256 / D;
-    const int d = tid % D, p = tid / D;
+    constexpr int PT = kQbarPairs / NP;  // pairs per thread
+    static_assert(D % 64 == 0, "a pair phase is a whole number of waves");
+    // the pair phase is wave-uniform: score_rows is then read with scalar loads
+    const int d = tid % D, p = __builtin_amdgcn_readfirstlane(tid / D);
     const int npairs = a.n_score_rows * a.G;
     const int i_end = min(npairs, (sp + 1) * kQbarPairs);
-    float acc = 0.f;
-#pragma unroll 8
-    for (int i = sp * kQbarPairs + p; i < i_end; i += NP) {
+    // pair indices clamped into range so every load is unconditional (no
+    // branch between a row index and its load); pairs past the range add 0
+    int off[PT];
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int i = min(sp * kQbarPairs + p + NP * u, npairs - 1);
       const int t = a.score_rows[i / a.G], j = i % a.G;
-      acc += (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + d];
+      off[u] = ((b * a.N + t) * a.Hq + g * a.G + j) * D;
     }
+    T x[PT];
+#pragma unroll
+    for (int u = 0; u < PT; ++u) x[u] = reinterpret_cast<const T*>(a.q)[(long long)off[u] + d];
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) acc += sp * kQbarPairs + p + NP * u < i_end ? (float)x[u] : 0.f;
     part[tid] = acc;
     __syncthreads();
     if (tid < D) {
@@ -1538,38 +1556,44 @@ __global__ void __launch_bounds__(256) verify_prep(const VerifyArgs a, int n_qba
     }
     return;
   }
+  // ancestor-or-self sets by pointer doubling: thread t owns node t (N <= 256),
+  // holding its set and jump in registers; each round publishes them to LDS
+  // and ORs in the set of the node it jumps to, whose jump it then takes
+  static_assert(kMaxNodes <= 256 && kAncWords == 8, "one node per thread, two 16-byte words per set");
   const int b = blockIdx.x - n_qbar_wgs;
   const int N = a.N;
-  for (int t = tid; t < N; t += 256) {
-    int p = a.parent[(long long)b * N + t];
-    if (p < 0 || p >= t) p = -1;  // malformed parents are treated as roots
-    jmp[0][t] = p;
+  const int t = tid;
+  const bool act = t < N;
+  int jp = act ? a.parent[(long long)b * N + t] : -1;
+  if (jp < 0 || jp >= t) jp = -1;  // malformed parents are treated as roots
+  uint32_t anc[kAncWords];
 #pragma unroll
-    for (int w = 0; w < kAncWords; ++w) {
-      uint32_t x = (w == (t >> 5)) ? (1u << (t & 31)) : 0u;
-      if (p >= 0 && w == (p >> 5)) x |= 1u << (p & 31);
-      ancs[0][t][w] = x;
-    }
+  for (int w = 0; w < kAncWords; ++w) {
+    uint32_t x = (act && w == (t >> 5)) ? (1u << (t & 31)) : 0u;
+    if (jp >= 0 && w == (jp >> 5)) x |= 1u << (jp & 31);
+    anc[w] = x;
   }
-  __syncthreads();
-  int cur = 0;
   for (int round = 0; round < 9; ++round) {
-    int any = 0;
-    for (int e = tid; e < N * kAncWords; e += 256) {
-      const int t = e / kAncWords, w = e % kAncWords;
-      const int j = jmp[cur][t];
-      ancs[cur ^ 1][t][w] = ancs[cur][t][w] | (j >= 0 ? ancs[cur][j][w] : 0u);
-      if (w == 0) {
-        const int jj = j >= 0 ? jmp[cur][j] : -1;
-        jmp[cur ^ 1][t] = jj;
-        any |= jj >= 0;
-      }
+    if (!__syncthreads_or(jp >= 0)) break;  // also: every read of the previous round is done
+    if (act) {
+      *reinterpret_cast<uint4*>(&ancs[t][0]) = uint4{anc[0], anc[1], anc[2], anc[3]};
+      *reinterpret_cast<uint4*>(&ancs[t][4]) = uint4{anc[4], anc[5], anc[6], anc[7]};
+      jmp[t] = jp;
     }
-    cur ^= 1;
-    if (!__syncthreads_or(any)) break;
+    __syncthreads();
+    if (jp >= 0) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(&ancs[jp][0]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(&ancs[jp][4]);
+      jp = jmp[jp];
+      anc[0] |= lo.x; anc[1] |= lo.y; anc[2] |= lo.z; anc[3] |= lo.w;
+      anc[4] |= hi.x; anc[5] |= hi.y; anc[6] |= hi.z; anc[7] |= hi.w;
+    }
   }
-  for (int e = tid; e < N * kAncWords; e += 256)
-    a.ws_anc[(long long)b * N * kAncWords + e] = ancs[cur][e / kAncWords][e % kAncWords];
+  if (act) {
+    uint4* dst = reinterpret_cast<uint4*>(a.ws_anc + ((long long)b * N + t) * kAncWords);
+    dst[0] = uint4{anc[0], anc[1], anc[2], anc[3]};
+    dst[1] = uint4{anc[4], anc[5], anc[6], anc[7]};
+  }
 }
 
 // ------------------------------------------------------------------------- host side
