@@ -270,6 +270,7 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
 // workgroup copies kCompactRows rows of one sequence as 16-byte pieces, every
 // load of a batch issued before any store.
 constexpr int kCompactRows = 16;
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 
 struct CompactArgs {
   KvView kv;
@@ -295,24 +296,27 @@ __global__ void __launch_bounds__(256) compact_rows(const CompactArgs a) {
   const char* kb = reinterpret_cast<const char*>(a.kv.k);
   const char* vb = reinterpret_cast<const char*>(a.kv.v);
   for (int base = 0; base < total; base += 256 * U) {
-    uint4 kx[U], vx[U];
+    // loads at clamped (always valid) pieces, all issued before the first store
+    u32x4 kx[U], vx[U];
     long long dst[U];
+    bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = base + tid + 256 * u;
-      const int r = e / a.row_pieces, c = e % a.row_pieces;
-      long long sl = -1;
-      if (e < total) sl = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + j0 + r]);
+      ok[u] = e < total;
+      const int ec = ok[u] ? e : total - 1;
+      const int r = ec / a.row_pieces, c = ec % a.row_pieces;
+      long long sl = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + j0 + r]);
       if (sl < 0) sl = 0;  // unmapped positions copy slot 0 (a caller-contract violation)
-      dst[u] = e < total ? ((long long)b * a.cap + j0 + r) * row_bytes + c * 16 : -1;
-      kx[u] = *reinterpret_cast<const uint4*>(kb + sl * row_bytes + c * 16);
-      vx[u] = *reinterpret_cast<const uint4*>(vb + sl * row_bytes + c * 16);
+      dst[u] = ((long long)b * a.cap + j0 + r) * row_bytes + c * 16;
+      kx[u] = *reinterpret_cast<const u32x4*>(kb + sl * row_bytes + c * 16);
+      vx[u] = *reinterpret_cast<const u32x4*>(vb + sl * row_bytes + c * 16);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (dst[u] >= 0) {
-        *reinterpret_cast<uint4*>(a.ck + dst[u]) = kx[u];
-        *reinterpret_cast<uint4*>(a.cv + dst[u]) = vx[u];
+      if (ok[u]) {
+        *reinterpret_cast<u32x4*>(a.ck + dst[u]) = kx[u];
+        *reinterpret_cast<u32x4*>(a.cv + dst[u]) = vx[u];
       }
     }
   }

@@ -1090,11 +1090,12 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   constexpr int LPW = RG::SEGS / NW;  // 1 KB copies per wave per stage
   static_assert(LPW * NW == RG::SEGS && LPW >= 1, "ring split over the waves");
   constexpr int QB4 = 4 * D * 2;      // score operand rows: qbar hi, mid, lo and a zero row
-  constexpr int LDS = RG::MAIN + RG::PT_CAP * 4 + RG::AUX_FLOATS * 4 + QB4;
+  constexpr int QSF = D + (NT / D) * D;  // qbar scratch: the sum, then one partial per pair phase
+  constexpr int LDS = RG::MAIN + RG::PT_CAP * 4 + QSF * 4 + QB4;
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   int* pt_lds = reinterpret_cast<int*>(smem + RG::MAIN);
   float* qs = reinterpret_cast<float*>(smem + RG::MAIN + RG::PT_CAP * 4);
-  T* qbt = reinterpret_cast<T*>(smem + RG::MAIN + RG::PT_CAP * 4 + RG::AUX_FLOATS * 4);
+  T* qbt = reinterpret_cast<T*>(smem + RG::MAIN + RG::PT_CAP * 4 + QSF * 4);
 
   // ---- workgroup -> (sequence, KV head, chunk, row block).  Chunk c runs on
   // XCD c % 8 (blockIdx % 8 picks the XCD), so every XCD gets a slice of every
