@@ -211,9 +211,6 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   const int bh = blockIdx.x * 4 + wave;
   if (bh >= a.B * a.Hq) return;
   const int b = bh / a.Hq;
-  int n = a.n_idx[a.per_head ? (long long)b * a.Hkv + (bh % a.Hq) / a.G : b];
-  n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
-  const int nc = (n + kChunk - 1) / kChunk;
   const long long rec0 = (long long)bh * a.n_chunks;
   constexpr int Q4 = D / 4;          // float4 column groups per row
   constexpr int CPL = 64 / Q4;       // chunks covered by one wave-wide load step
@@ -221,14 +218,32 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
   const int quad = lane % Q4, sub = lane / Q4;
   float m = kNegInf, lsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int cb = 0; cb < nc; cb += CPL * STEPS) {
-    f32x4 x[STEPS];
-    f32x2 ml[STEPS];
+  f32x4 x[STEPS];
+  f32x2 ml[STEPS];
+  // a batch of chunks, loaded unconditionally at indices clamped into the
+  // workspace (a guarded load would wait for its predecessor); records past
+  // the count hold stale data and are selected away below
+  auto fetch = [&](int cb) {
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) {
-      const int c = cb + j * CPL + sub;
-      x[j] = c < nc ? *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * quad) : f32x4{0.f, 0.f, 0.f, 0.f};
-      ml[j] = c < nc ? a.ws_ml[rec0 + c] : f32x2{kNegInf, 0.f};
+      const int c = min(cb + j * CPL + sub, a.n_chunks - 1);
+      x[j] = *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * quad);
+      ml[j] = a.ws_ml[rec0 + c];
+    }
+  };
+  // the first batch is requested before the count: the loads do not wait for it
+  fetch(0);
+  int n = a.n_idx[a.per_head ? (long long)b * a.Hkv + (bh % a.Hq) / a.G : b];
+  n = n < 0 ? 0 : (n > a.max_idx ? a.max_idx : n);
+  const int nc = (n + kChunk - 1) / kChunk;
+  for (int cb = 0;;) {
+    // records past the count are selected away unread
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+      if (cb + j * CPL + sub >= nc) {
+        x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ml[j] = f32x2{kNegInf, 0.f};
+      }
     }
     float bm = m;
 #pragma unroll
@@ -243,6 +258,9 @@ __global__ void __launch_bounds__(256) sparse_merge(const SparseArgs a) {
       lsum += w * ml[j][1];
     }
     m = bm;
+    cb += CPL * STEPS;
+    if (cb >= nc) break;
+    fetch(cb);
   }
   // lanes with the same quad (different sub) hold different chunks
   const float M = wave_max(m);
