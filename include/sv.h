@@ -21,6 +21,8 @@
  *                         sink + recent-window baseline.
  *   sv_build_tree         best-first draft tree (parent array) from per-depth
  *                         draft log-probabilities.
+ *   sv_validate_kv, sv_validate_tree, sv_validate_index   checks of the
+ *                         device-array contract (debugging aids).
  *   sv_accept_commit      greedy acceptance of the verified drafts and the
  *                         accepted branch's K/V moved behind the prefix.
  *
@@ -312,6 +314,37 @@ sv_status sv_accept_commit(sv_dtype dtype, int B, int N, int Hkv, int D, const s
                            const int32_t* prefix_len, int P_max, const int32_t* parent,
                            const int32_t* draft_tokens, const int32_t* target_tokens, int32_t* path,
                            int32_t* n_accepted, int32_t* bonus, int32_t* new_prefix_len, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Contract checks of device arrays (debugging aids, not steps of the method).
+ *
+ * The calls above trust the contents of their device arrays; a violation
+ * gives unspecified results, never an access outside the caller's buffers.
+ * These calls check those contents on `stream` (asynchronously, allocating
+ * nothing) and write an error record to `err`, a device int32[4]
+ * {code, b, i, value}: all zeros when every check passes, otherwise ONE of
+ * the violations found (which one is unspecified when there are several).
+ * Read `err` after the stream has reached the call.  Codes:
+ *   1  prefix_len[b] = value lies outside [0, P_max];
+ *   2  logical position i of sequence b (i < P_b + N) maps to no slot in
+ *      [0, num_slots) (value: its page-table entry, or -1);
+ *   3  parent[b][i] = value: the root's is not -1, or another's is not in [0, i);
+ *   4  n_idx of list b = value lies outside [0, max_idx];
+ *   5  entry i of list b is position value, negative or mapped to no slot.
+ *
+ * sv_validate_kv:    prefix lengths and the mapping of positions [0, P_b + N)
+ *                    (the ranges sv_verify_attn reads; N = 0 for the prefix).
+ * sv_validate_tree:  the parent arrays of sv_verify_attn / sv_accept_commit.
+ * sv_validate_index: index lists of the sparse draft step: B * lists_per_seq
+ *                    lists ([B][lists_per_seq][idx_stride], 1 list per
+ *                    sequence or Hkv for the per-head variant) and their counts.
+ * Errors: SV_E_INVALID for a NULL or misaligned err, NULL arrays or bad sizes;
+ * SV_E_UNSUPPORTED for more than 65535 sequences or lists. */
+sv_status sv_validate_kv(int B, int N, const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                         int32_t* err, sv_stream stream);
+sv_status sv_validate_tree(int B, int N, const int32_t* parent, int32_t* err, sv_stream stream);
+sv_status sv_validate_index(int B, int lists_per_seq, const sv_kv_cache* kv, const int32_t* idx, int idx_stride,
+                            const int32_t* n_idx, int max_idx, int32_t* err, sv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* Optional timing hook for profiling: while set (non-NULL), every

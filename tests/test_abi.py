@@ -211,3 +211,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_validators_reject_bad_arguments():
+    """sv_validate_*: the error record must be a non-NULL aligned device
+    pointer, sizes non-negative, arrays present; all checked before launching."""
+    lib = _lib.load()
+    kv = _kv()
+    assert lib.sv_validate_kv(2, 8, ctypes.byref(kv), FAKE, 100, None, None) == 1
+    assert lib.sv_validate_kv(2, 8, ctypes.byref(kv), FAKE, 100, FAKE + 2, None) == 1
+    assert "aligned" in lib.sv_last_error().decode()
+    assert lib.sv_validate_kv(-1, 8, ctypes.byref(kv), FAKE, 100, FAKE, None) == 1
+    assert lib.sv_validate_kv(2, 8, ctypes.byref(kv), None, 100, FAKE, None) == 1
+    assert lib.sv_validate_kv(2, 8, None, FAKE, 100, FAKE, None) == 1
+    assert lib.sv_validate_kv(70000, 8, ctypes.byref(kv), FAKE, 100, FAKE, None) == 2
+    assert lib.sv_validate_tree(2, 8, None, FAKE, None) == 1
+    assert lib.sv_validate_tree(2, -1, FAKE, FAKE, None) == 1
+    assert lib.sv_validate_tree(2, 8, FAKE, None, None) == 1
+    assert lib.sv_validate_index(2, 0, ctypes.byref(kv), FAKE, 64, FAKE, 64, FAKE, None) == 1
+    assert lib.sv_validate_index(2, 1, ctypes.byref(kv), FAKE, 32, FAKE, 64, FAKE, None) == 1
+    assert lib.sv_validate_index(2, 1, ctypes.byref(kv), FAKE, 64, None, 64, FAKE, None) == 1
+    assert lib.sv_validate_index(40000, 8, ctypes.byref(kv), FAKE, 64, FAKE, 64, FAKE, None) == 2

@@ -16,6 +16,7 @@ from __future__ import annotations
 import ctypes
 import dataclasses
 import math
+import os
 from typing import Optional, Sequence
 
 import torch
@@ -26,7 +27,8 @@ from ._lib import SvError, SV_F32, SV_BF16  # noqa: F401
 __all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_attn", "compact_kv",
            "dense_draft_attn", "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size",
            "dense_draft_workspace_size", "build_tree", "accept_commit", "verify_attn_per_head",
-           "sparse_draft_attn_per_head", "select_sink_window", "timing_events", "SvError", "lib"]
+           "sparse_draft_attn_per_head", "select_sink_window", "timing_events", "SvError", "lib",
+           "validate_kv", "validate_tree", "validate_index", "ContractError"]
 
 
 def lib() -> ctypes.CDLL:
@@ -142,6 +144,10 @@ def verify_attn(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max
                                    kv.page_size if kv.page_table is not None else 0)
     wptr, wlen = _ws(workspace, "verify").get(nbytes, q.device)
     kvs = kv.c_struct()
+    if _debug_checks():
+        _raise_on(validate_kv(kv, prefix_len, P_max=P_max, N=N))
+        if parent is not None:
+            _raise_on(validate_tree(parent))
     _lib.check(L.sv_verify_attn(_ptr(q), dt, B, N, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(prefix_len), P_max,
                                 _ptr(parent), rows_arr, len(rows), float(scale), _ptr(out),
                                 _ptr(scores) if rows else None, wptr, wlen, _stream(q.device)))
@@ -182,6 +188,8 @@ def sparse_draft_attn(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, n_idx: to
     nbytes = sparse_workspace_size(B, Hq, kv.Hkv, D, max_idx)
     wptr, wlen = _ws(workspace, "sparse").get(nbytes, q.device)
     kvs = kv.c_struct()
+    if _debug_checks():
+        _raise_on(validate_index(kv, idx, n_idx, max_idx=max_idx))
     _lib.check(L.sv_sparse_draft_attn(_ptr(q), dt, B, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(idx), stride,
                                       _ptr(n_idx), max_idx, float(scale), _ptr(out), wptr, wlen,
                                       _stream(q.device)))
@@ -225,6 +233,8 @@ def sparse_draft_attn_per_head(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, 
     dt = _dtype_code(q)
     wptr, wlen = _ws(workspace, "sparse").get(sparse_workspace_size(B, Hq, kv.Hkv, D, max_idx), q.device)
     kvs = kv.c_struct()
+    if _debug_checks():
+        _raise_on(validate_index(kv, idx, n_idx, max_idx=max_idx))
     _lib.check(L.sv_sparse_draft_attn_per_head(_ptr(q), dt, B, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(idx), stride,
                                                _ptr(n_idx), max_idx, float(scale), _ptr(out), wptr, wlen,
                                                _stream(q.device)))
@@ -343,3 +353,72 @@ class timing_events:
 
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+# ---------------------------------------------------------------------------
+# Device-array contract checks (sv_validate_*).  Each returns the error record
+# (code, b, i, value) as host ints after synchronising the stream; (0, 0, 0, 0)
+# means every check passed.  With SV_DEBUG_CHECKS=1 in the environment,
+# verify_attn and sparse_draft_attn run them first and raise ContractError.
+
+_CONTRACT = {
+    1: "prefix_len[{b}] = {v} lies outside [0, P_max]",
+    2: "position {i} of sequence {b} maps to no KV slot (page entry {v})",
+    3: "parent[{b}][{i}] = {v} is not a valid parent",
+    4: "n_idx of list {b} = {v} lies outside [0, max_idx]",
+    5: "entry {i} of index list {b} is position {v}, negative or mapped to no KV slot",
+}
+
+
+class ContractError(ValueError):
+    """A device array violates the documented contract of an entry point."""
+
+
+def _debug_checks() -> bool:
+    return os.environ.get("SV_DEBUG_CHECKS", "") == "1"
+
+
+def _raise_on(rec) -> None:
+    code, b, i, v = rec
+    if code:
+        raise ContractError(_CONTRACT.get(code, "contract violation {c}").format(b=b, i=i, v=v, c=code))
+
+
+def _err_record(dev: torch.device):
+    return torch.empty((4,), dtype=torch.int32, device=dev)
+
+
+def _read_record(err: torch.Tensor):
+    torch.cuda.current_stream(err.device).synchronize()
+    return tuple(int(x) for x in err.cpu().tolist())
+
+
+def validate_kv(kv: KVCache, prefix_len: torch.Tensor, *, P_max: int, N: int = 0):
+    """sv_validate_kv: prefix lengths in [0, P_max], positions [0, P_b + N) mapped to slots."""
+    err = _err_record(prefix_len.device)
+    kvs = kv.c_struct()
+    B = int(prefix_len.shape[0])
+    _lib.check(lib().sv_validate_kv(B, int(N), ctypes.byref(kvs), _ptr(prefix_len), int(P_max), _ptr(err),
+                                    _stream(prefix_len.device)))
+    return _read_record(err)
+
+
+def validate_tree(parent: torch.Tensor):
+    """sv_validate_tree: parent [B][N], root -1, every other parent in [0, i)."""
+    err = _err_record(parent.device)
+    B, N = (int(x) for x in parent.shape)
+    _lib.check(lib().sv_validate_tree(B, N, _ptr(parent), _ptr(err), _stream(parent.device)))
+    return _read_record(err)
+
+
+def validate_index(kv: KVCache, idx: torch.Tensor, n_idx: torch.Tensor, *, max_idx: Optional[int] = None):
+    """sv_validate_index: idx [B][stride] (or [B][Hkv][stride]), counts n_idx [B] (or [B][Hkv])."""
+    err = _err_record(idx.device)
+    kvs = kv.c_struct()
+    B = int(idx.shape[0])
+    per_seq = int(idx.shape[1]) if idx.dim() == 3 else 1
+    stride = int(idx.shape[-1])
+    max_idx = stride if max_idx is None else int(max_idx)
+    _lib.check(lib().sv_validate_index(B, per_seq, ctypes.byref(kvs), _ptr(idx), stride, _ptr(n_idx), max_idx,
+                                       _ptr(err), _stream(idx.device)))
+    return _read_record(err)

@@ -19,6 +19,7 @@ EXPORTS = (
     "sv_verify_attn_per_head", "sv_sparse_draft_attn_per_head", "sv_select_sink_window",
     "sv_compact_kv", "sv_dense_draft_workspace_size", "sv_dense_draft_attn", "sv_build_tree",
     "sv_accept_commit",
+    "sv_validate_kv", "sv_validate_tree", "sv_validate_index",
     "sv_set_verify_timing_events",
 )
 
@@ -56,6 +57,12 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     kvp = ctypes.POINTER(SvKvCache)
+    lib.sv_validate_kv.restype = i32
+    lib.sv_validate_kv.argtypes = [i32, i32, kvp, vp, i32, vp, vp]
+    lib.sv_validate_tree.restype = i32
+    lib.sv_validate_tree.argtypes = [i32, i32, vp, vp, vp]
+    lib.sv_validate_index.restype = i32
+    lib.sv_validate_index.argtypes = [i32, i32, kvp, vp, i32, vp, i32, vp, vp]
     lib.sv_abi_version.restype = i32
     lib.sv_abi_version.argtypes = []
     lib.sv_last_error.restype = ctypes.c_char_p

@@ -335,3 +335,50 @@ sv_status sv_build_tree(int B, int n_nodes, int max_depth, int n_cand, const dou
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Contract checks of device arrays (debugging aids; asynchronous, allocate nothing).
+
+namespace {
+sv_status check_err_ptr(const int32_t* err) {
+  if (!err) return fail(SV_E_INVALID, "err must be a device int32[4]");
+  if (reinterpret_cast<uintptr_t>(err) & 3) return fail(SV_E_INVALID, "err must be 4-byte aligned");
+  return SV_OK;
+}
+}  // namespace
+
+extern "C" sv_status sv_validate_kv(int B, int N, const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                                    int32_t* err, sv_stream stream) {
+  sv_status st;
+  if ((st = check_err_ptr(err))) return st;
+  if (B < 0 || N < 0 || P_max < 0) return fail(SV_E_INVALID, "B, N and P_max must be >= 0");
+  if (B > 65535) return fail(SV_E_UNSUPPORTED, "B > 65535");
+  if (B > 0 && !prefix_len) return fail(SV_E_INVALID, "prefix_len is NULL");
+  if ((st = check_kv(kv, B))) return st;
+  return hip_status(sv::launch_validate_kv(B, N, kv_args(kv), prefix_len, P_max, err, stream), "sv_validate_kv launch");
+}
+
+extern "C" sv_status sv_validate_tree(int B, int N, const int32_t* parent, int32_t* err, sv_stream stream) {
+  sv_status st;
+  if ((st = check_err_ptr(err))) return st;
+  if (B < 0 || N < 0) return fail(SV_E_INVALID, "B and N must be >= 0");
+  if (B > 65535) return fail(SV_E_UNSUPPORTED, "B > 65535");
+  if (B > 0 && N > 0 && !parent) return fail(SV_E_INVALID, "parent is NULL");
+  return hip_status(sv::launch_validate_tree(B, N, parent, err, stream), "sv_validate_tree launch");
+}
+
+extern "C" sv_status sv_validate_index(int B, int lists_per_seq, const sv_kv_cache* kv, const int32_t* idx,
+                                       int idx_stride, const int32_t* n_idx, int max_idx, int32_t* err,
+                                       sv_stream stream) {
+  sv_status st;
+  if ((st = check_err_ptr(err))) return st;
+  if (B < 0 || lists_per_seq < 1) return fail(SV_E_INVALID, "need B >= 0 and lists_per_seq >= 1");
+  if (max_idx < 0 || idx_stride < max_idx) return fail(SV_E_INVALID, "need 0 <= max_idx <= idx_stride");
+  const long long lists = (long long)B * lists_per_seq;
+  if (lists > 65535) return fail(SV_E_UNSUPPORTED, "more than 65535 index lists");
+  if (lists > 0 && (!n_idx || (!idx && max_idx > 0))) return fail(SV_E_INVALID, "idx and n_idx must be non-NULL");
+  if ((st = check_kv(kv, B))) return st;
+  return hip_status(sv::launch_validate_index((int)lists, lists_per_seq, kv_args(kv), idx, idx_stride, n_idx, max_idx,
+                                              err, stream),
+                    "sv_validate_index launch");
+}

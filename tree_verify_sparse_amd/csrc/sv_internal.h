@@ -80,4 +80,16 @@ int launch_sparse(const SparsePlan& p, int dtype, const void* q, const KvArgs& k
 int launch_sink_window(int B, int P_max, const int32_t* prefix_len, int sink, int window, int k_max, int32_t* idx,
                        int32_t* count, void* stream);
 
+// Contract checks of device arrays (error record {code, b, i, value}; codes below).
+constexpr int kErrPrefixLen = 1;  // prefix_len[b] = value outside [0, P_max]
+constexpr int kErrUnmapped = 2;   // position i of sequence b maps to no slot (value: its page entry, or -1)
+constexpr int kErrParent = 3;     // parent[b][i] = value is not -1 for the root / not in [0, i)
+constexpr int kErrCount = 4;      // n_idx[list b] = value outside [0, max_idx]
+constexpr int kErrIndex = 5;      // entry i of list b is position value, negative or mapped to no slot
+int launch_validate_kv(int B, int N, const KvArgs& kv, const int32_t* prefix_len, int P_max, int32_t* err,
+                       void* stream);
+int launch_validate_tree(int B, int N, const int32_t* parent, int32_t* err, void* stream);
+int launch_validate_index(int n_lists, int lists_per_seq, const KvArgs& kv, const int32_t* idx, int idx_stride,
+                          const int32_t* n_idx, int max_idx, int32_t* err, void* stream);
+
 }  // namespace sv
