@@ -328,6 +328,44 @@ def main():
         torch.cuda.synchronize()
         build_us = e0.elapsed_time(e1) * 1e3 / K
 
+    # tokens-per-time projection (KnapSpec §2) for chains, from this layer's
+    # measured times: t_target = verification with selection (and the
+    # compaction on that path), t_draft = one draft decode; gamma = the chain's
+    # drafted tokens.  One attention layer only: the projection leaves out the
+    # models' other layers and MLPs, and alpha is assumed, not measured.
+    tpt_rows = None
+    if wl.parent is None and n_draft > 0:
+        def timed(fn):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(K):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / K
+
+        def target(i):
+            c = i % copies
+            st = f_verify(*vargs[c]) | f_topk(*targs)
+            if draft_path == "compact":
+                st |= f_compact(*cargs[c])
+            if st:
+                raise RuntimeError(L.sv_last_error().decode())
+
+        def draft(i):
+            st = f_dense(*ddargs[0]) if draft_path == "compact" else f_sparse(*dargs[i % copies][0])
+            if st:
+                raise RuntimeError(L.sv_last_error().decode())
+
+        t_target, t_draft = timed(target), timed(draft)
+        gamma = wl.N - 1
+        tpt_rows = {"gamma": gamma, "t_target_us": round(t_target, 2), "t_draft_us": round(t_draft, 2),
+                    "tokens_per_ms": {f"alpha={a}": round(tpt(a, gamma, t_draft, t_target) * 1e3, 2)
+                                      for a in (0.6, 0.7, 0.8, 0.9)},
+                    "scope": "one attention layer (verify + selection, one draft decode); assumed alpha"}
+
     value = step_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": "verify+select+sparse-draft us/step and HBM GB/s (% peak) at 32k ctx, 1 GPU",
@@ -347,7 +385,8 @@ def main():
         "roofline": roof,
         "next_rows": {"accept_commit_us": round(accept_us, 2),
                       "accepted_mean": round(float(an.float().mean().item()), 2),
-                      "build_tree_us": round(build_us, 2) if build_us is not None else None},
+                      "build_tree_us": round(build_us, 2) if build_us is not None else None,
+                      "tpt_projection": tpt_rows},
     }
     if not args.no_cpu_baseline and args.workload in (1, 2, 3):
         res["cpu_baseline"] = cpu_baseline(wl, step_bytes, args.cpu_seconds)
@@ -369,6 +408,14 @@ def _traffic(workload: int):
     except OSError:
         pass
     return None
+
+
+def tpt(alpha: float, gamma: int, t_draft: float, t_target: float) -> float:
+    """Tokens per unit of time of a draft-verify round (KnapSpec §2, the TPT
+    metric): (1 - alpha^(gamma+1)) / (1 - alpha) expected tokens (gamma + 1 at
+    alpha = 1) over gamma draft steps and one target pass."""
+    tokens = gamma + 1.0 if alpha == 1.0 else (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
+    return tokens / (gamma * t_draft + t_target)
 
 
 def cpu_baseline(wl, step_bytes, target_s):

@@ -13,6 +13,7 @@ the path computes, each function citing the passage it follows.  Sources cited
 * "Vegas" (2602.07223) -- Resumo Técnico: Vegas, Decodificação Auto-Especulativa
   com Atenção Esparsa Guiada por Verificação.
 * "JETFLOW" (2606.18394) -- Resumo Técnico: JETFLOW.
+* "KnapSpec" (2602.20217) -- Resumo Técnico: KnapSpec (§2, the tokens-per-time metric).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed forms,
 brute force, library routines and invariants; see ``oracle/reference.py``'s
@@ -37,4 +38,5 @@ from .reference import (  # noqa: F401
     commit_accepted_kv,
     run_step,
     bf16_bits_to_f64,
+    tpt,
 )

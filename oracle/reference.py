@@ -44,6 +44,9 @@ Pins (tests/test_oracle_*.py):
                           trees (the deepest node whose whole branch matches)
   commit_accepted_kv   -- every moved row equals its source row, nothing else
                           changes
+  tpt                  -- alpha = 0, alpha = 1 and gamma = 0 closed forms; the
+                          expected-token factor == an explicit sum of alpha^i
+                          for i = 0..gamma
   compact_kv, dense_draft_attention -- compacted rows == sparse_draft_attention
                           over the same list; a tail == the tail rows placed in
                           a cache past the prefix and listed; one row == its V
@@ -467,3 +470,19 @@ def run_step(wl, rows=None, decode_step: int = 0, with_attention: bool = True) -
     if wl.dq.shape[0] > decode_step:
         res["draft"] = sparse_draft_attention(wl.dq[decode_step], wl.dtype, kv, res["idx"], wl.scale, wl.Hkv)
     return res
+
+
+# ----------------------------------------------------------------------------
+# Tokens per time (KnapSpec §2, the TPT metric): with acceptance rate alpha and
+# draft length gamma, a draft-verify round yields (1 - alpha^(gamma+1)) /
+# (1 - alpha) tokens in expectation and costs gamma draft steps plus one
+# target (verification) pass.  At alpha = 1 the factor is its limit gamma + 1.
+
+def tpt(alpha: float, gamma: int, t_draft: float, t_target: float) -> float:
+    """Tokens per unit of time (the unit of t_draft and t_target)."""
+    alpha = float(alpha)
+    if alpha == 1.0:
+        tokens = float(gamma + 1)
+    else:
+        tokens = (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
+    return tokens / (gamma * float(t_draft) + float(t_target))

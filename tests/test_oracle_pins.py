@@ -561,3 +561,21 @@ def test_sink_window_select_by_hand():
     assert oracle.sink_window_select(4, 2, 3).tolist() == [0, 1, 2, 3]      # overlap
     assert oracle.sink_window_select(0, 2, 3).tolist() == []
     assert oracle.sink_window_select(100, 0, 5).tolist() == [95, 96, 97, 98, 99]
+
+
+# ---- tokens per time (KnapSpec §2 TPT metric)
+
+def test_tpt_closed_forms_and_series():
+    """alpha = 0: one token per round; alpha = 1: gamma + 1 tokens (the
+    limit); gamma = 0: one token per target pass; otherwise the token factor
+    is the explicit sum of alpha^i over i = 0..gamma."""
+    assert oracle.tpt(0.0, 7, 3.0, 50.0) == pytest.approx(1.0 / (7 * 3.0 + 50.0), rel=1e-15)
+    assert oracle.tpt(1.0, 7, 3.0, 50.0) == pytest.approx(8.0 / (7 * 3.0 + 50.0), rel=1e-15)
+    assert oracle.tpt(0.7, 0, 3.0, 50.0) == pytest.approx(1.0 / 50.0, rel=1e-15)
+    for alpha in (0.1, 0.5, 0.8, 0.95, 0.999999):
+        for gamma in (1, 3, 7, 15):
+            tokens = sum(alpha ** i for i in range(gamma + 1))
+            assert oracle.tpt(alpha, gamma, 2.5, 40.0) == pytest.approx(tokens / (gamma * 2.5 + 40.0), rel=1e-9)
+    # more acceptance never lowers the rate; a slower draft always lowers it
+    assert oracle.tpt(0.9, 7, 3.0, 50.0) > oracle.tpt(0.8, 7, 3.0, 50.0)
+    assert oracle.tpt(0.8, 7, 4.0, 50.0) < oracle.tpt(0.8, 7, 3.0, 50.0)
