@@ -127,7 +127,7 @@ __device__ __forceinline__ void barrier_only() { __builtin_amdgcn_s_barrier(); }
 __device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(l), "v"(src) : "memory");  // streamed: non-temporal
 }
 
 // K/V storage addressing: logical position -> slot; out-of-range -> -1.

@@ -624,12 +624,14 @@ struct WaveRing {
 
 // One 16-byte-per-lane global->LDS copy (1 KB per wave).  `lds` is the
 // wave-uniform LDS byte address, `off` a per-lane 32-bit offset from the
-// wave-uniform base `base` (the scalar-base form of the instruction).
+// wave-uniform base `base` (the scalar-base form of the instruction).  The
+// copies carry the non-temporal hint: K/V is streamed, and the hint took the
+// 32k step from 63.6 to 59.2 us (the 4 x 128k batch from 769 to 697 us).
 __device__ __forceinline__ void dma16_sbase(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(off), "s"(base) : "memory");
 }
 __device__ __forceinline__ void dma16_vaddr(uint32_t lds, const void* addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(addr) : "memory");
 }
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in {0, step, 2 step, 3 step}
