@@ -130,3 +130,28 @@ def test_record_is_cleared_between_calls_and_debug_env(monkeypatch):
         sv.verify_attn(dw.q, dw.kv, i32(P), P_max=wl.P_max, parent=dw.parent, score_rows=[0])
     out, _ = sv.verify_attn(dw.q, dw.kv, dw.P, P_max=wl.P_max, parent=dw.parent, score_rows=[0])
     assert torch.isfinite(out.float()).all()
+
+
+def test_debug_checks_stay_out_of_graph_capture(monkeypatch):
+    """With SV_DEBUG_CHECKS=1 an eager call is checked, while a call captured in
+    a HIP graph is not (the checks synchronise); the captured call replays."""
+    wl = _wl(False, tree=False)
+    dw = DevWorkload(wl)
+    monkeypatch.setenv("SV_DEBUG_CHECKS", "1")
+    _, _, idx, count, _ = dw.step()
+    out = torch.empty_like(dw.dq[0])
+    ws = sv.Workspace()
+    sv.sparse_draft_attn(dw.dq[0], dw.kv, idx, count, max_idx=wl.k_max, out=out, workspace=ws)
+    ref = out.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.sparse_draft_attn(dw.dq[0], dw.kv, idx, count, max_idx=wl.k_max, out=out, workspace=ws)
+    out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    bad = count.clone()
+    bad[0] = wl.k_max + 1
+    with pytest.raises(sv.ContractError, match="n_idx"):
+        sv.sparse_draft_attn(dw.dq[0], dw.kv, idx, bad, max_idx=wl.k_max, out=out, workspace=ws)

@@ -359,7 +359,8 @@ def default_scale(D: int) -> float:
 # Device-array contract checks (sv_validate_*).  Each returns the error record
 # (code, b, i, value) as host ints after synchronising the stream; (0, 0, 0, 0)
 # means every check passed.  With SV_DEBUG_CHECKS=1 in the environment,
-# verify_attn and sparse_draft_attn run them first and raise ContractError.
+# verify_attn and sparse_draft_attn run them first (except under graph
+# capture) and raise ContractError.
 
 _CONTRACT = {
     1: "prefix_len[{b}] = {v} lies outside [0, P_max]",
@@ -375,7 +376,9 @@ class ContractError(ValueError):
 
 
 def _debug_checks() -> bool:
-    return os.environ.get("SV_DEBUG_CHECKS", "") == "1"
+    # the checks synchronise, which a stream under graph capture does not allow:
+    # captured calls are not checked
+    return os.environ.get("SV_DEBUG_CHECKS", "") == "1" and not torch.cuda.is_current_stream_capturing()
 
 
 def _raise_on(rec) -> None:
