@@ -333,18 +333,45 @@ def main():
     # compaction on that path), t_draft = one draft decode; gamma = the chain's
     # drafted tokens.  One attention layer only: the projection leaves out the
     # models' other layers and MLPs, and alpha is assumed, not measured.
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
+
+    def select_only(i):
+        if f_topk(*targs):
+            raise RuntimeError(L.sv_last_error().decode())
+
+    def draft_only(i):
+        st = f_dense(*ddargs[0]) if draft_path == "compact" else f_sparse(*dargs[i % copies][0])
+        if st:
+            raise RuntimeError(L.sv_last_error().decode())
+
+    # the selection and one draft decode on their own (after a full step, so the
+    # scores and the selected set are current), against the HBM roof: their
+    # algorithmic bytes per call over the call's time (launch included)
+    step(0)
+    select_us = timed(select_only)
+    per_draft_bytes = draft_bytes // n_draft if n_draft > 0 else 0
+    draft_us = timed(draft_only) if n_draft > 0 else None
+    other_roofs = {
+        "select": {"us": round(select_us, 2), "algorithmic_bytes": select_bytes,
+                   "achieved_GBs": round(select_bytes / select_us / 1e3, 1),
+                   "frac": round(select_bytes / select_us / 1e3 / HBM_PEAK_GBS, 5)},
+        "draft_decode": None if draft_us is None else {
+            "us": round(draft_us, 2), "algorithmic_bytes": per_draft_bytes,
+            "achieved_GBs": round(per_draft_bytes / draft_us / 1e3, 1),
+            "frac": round(per_draft_bytes / draft_us / 1e3 / HBM_PEAK_GBS, 4)},
+    }
+
     tpt_rows = None
     if wl.parent is None and n_draft > 0:
-        def timed(fn):
-            for i in range(3):
-                fn(i)
-            torch.cuda.synchronize()
-            e0.record()
-            for i in range(K):
-                fn(i)
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / K
 
         def target(i):
             c = i % copies
@@ -354,12 +381,7 @@ def main():
             if st:
                 raise RuntimeError(L.sv_last_error().decode())
 
-        def draft(i):
-            st = f_dense(*ddargs[0]) if draft_path == "compact" else f_sparse(*dargs[i % copies][0])
-            if st:
-                raise RuntimeError(L.sv_last_error().decode())
-
-        t_target, t_draft = timed(target), timed(draft)
+        t_target, t_draft = timed(target), draft_us
         gamma = wl.N - 1
         tpt_rows = {"gamma": gamma, "t_target_us": round(t_target, 2), "t_draft_us": round(t_draft, 2),
                     "tokens_per_ms": {f"alpha={a}": round(tpt(a, gamma, t_draft, t_target) * 1e3, 2)
@@ -386,7 +408,8 @@ def main():
         "next_rows": {"accept_commit_us": round(accept_us, 2),
                       "accepted_mean": round(float(an.float().mean().item()), 2),
                       "build_tree_us": round(build_us, 2) if build_us is not None else None,
-                      "tpt_projection": tpt_rows},
+                      "tpt_projection": tpt_rows,
+                      "select_and_draft_rooflines": other_roofs},
     }
     if not args.no_cpu_baseline and args.workload in (1, 2, 3):
         res["cpu_baseline"] = cpu_baseline(wl, step_bytes, args.cpu_seconds)
