@@ -55,6 +55,17 @@ CASES = {
         seed=111, B=2, Hq=8, Hkv=2, D=128, dtype="bf16", P=[0, 5], N=4, score_rows="all", k_sel=10),
     "no_scores": lambda: make_custom(
         seed=112, B=1, Hq=8, Hkv=2, D=128, dtype="bf16", P=900, N=6, score_rows=[], k_sel=10, decode_steps=0),
+    # head_dim 64 tree kernel (96 rows per KV head), paged, ragged prefixes
+    "tree24_bf16_d64_paged": lambda: make_custom(
+        seed=113, B=3, Hq=16, Hkv=4, D=64, dtype="bf16", P=[1500, 77, 640], N=24, tree="best_first",
+        tree_depth=5, score_rows="all", k_sel=60, layout="paged", page_size=16),
+    # small trees on the streaming kernel: 48 and 64 rows per KV head (two row tiles)
+    "tree12_stream_g4": lambda: make_custom(
+        seed=114, B=2, Hq=16, Hkv=4, D=128, dtype="bf16", P=[2100, 513], N=12, tree="best_first",
+        tree_depth=4, score_rows="c2q", k_sel=90),
+    "tree64_stream_mha": lambda: make_custom(
+        seed=115, B=1, Hq=4, Hkv=4, D=128, dtype="bf16", P=1900, N=64, tree="best_first", tree_depth=6,
+        score_rows="all", k_sel=120),
 }
 
 
