@@ -1388,13 +1388,15 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   const float lt = half_sum(l);
   if (row_ok) {
     const long long rec = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks + c;
-    float* dst = a.ws_o + rec * D;
+    // o partials in bf16 (relative rounding 2^-9, far inside the output
+    // tolerance): the merge then reads half the bytes
+    bf16* dst = reinterpret_cast<bf16*>(a.ws_o) + rec * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * qd + 4 * h) =
-            f32x4{o[db][4 * qd], o[db][4 * qd + 1], o[db][4 * qd + 2], o[db][4 * qd + 3]};
+        *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * qd + 4 * h) =
+            bf16x4{(bf16)o[db][4 * qd], (bf16)o[db][4 * qd + 1], (bf16)o[db][4 * qd + 2], (bf16)o[db][4 * qd + 3]};
     if (h == 0) a.ws_ml[rec] = f32x2{m, lt};
   }
 }
@@ -1423,7 +1425,7 @@ __device__ __forceinline__ MergeAcc merge_acc(const MergeAcc& x, const MergeAcc&
   return MergeAcc{M, wx * x.l + wy * y.l, wx * x.o + wy * y.o};
 }
 
-template <typename T, int D>
+template <typename T, int D, bool OB>
 __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_row_wgs, int wpr) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < n_row_wgs) {
@@ -1455,7 +1457,14 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
         const int c = c0 + 2 * wpr * u;
         const bool ok = c < nc;
         ml[u] = ok ? a.ws_ml[rec0 + c] : f32x2{kNegInf, 0.f};
-        ov[u] = ok ? *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * qc) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (OB) {
+          const bf16x4 x = ok ? *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(a.ws_o) +
+                                                                  (rec0 + c) * D + 4 * qc)
+                              : bf16x4{};
+          ov[u] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+        } else {
+          ov[u] = ok ? *reinterpret_cast<const f32x4*>(a.ws_o + (rec0 + c) * D + 4 * qc) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
       float bm = acc.m;
 #pragma unroll
@@ -1762,7 +1771,10 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
   const int wpr = p.n_chunks >= 16 ? 4 : 1;  // waves per merged row
   const int n_row_wgs = (p.B * p.Hkv * p.R * wpr + 3) / 4;
   const long long n_s = p.scores ? ((long long)p.B * p.P_max + 255) / 256 : 0;
-  hipLaunchKernelGGL((verify_merge<T, D>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
+  if (p.treek)  // the tree kernel writes its o partials in bf16
+    hipLaunchKernelGGL((verify_merge<T, D, true>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
+  else
+    hipLaunchKernelGGL((verify_merge<T, D, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
   return (int)hipGetLastError();
 }
 
