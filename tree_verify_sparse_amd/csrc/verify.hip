@@ -1058,7 +1058,9 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       if (row < a.R) {
         const long long rec = ((long long)(b * a.Hkv + g) * a.Rpad + row) * a.n_chunks + c;
 #pragma unroll
-        for (int i = 0; i < CPT / 4; ++i) *reinterpret_cast<f32x4*>(a.ws_o + rec * D + cg * CPT + 4 * i) = acc[i];
+        for (int i = 0; i < CPT / 4; ++i)  // bf16 partials, as the tree kernel's
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.ws_o) + rec * D + cg * CPT + 4 * i) =
+              bf16x4{(bf16)acc[i][0], (bf16)acc[i][1], (bf16)acc[i][2], (bf16)acc[i][3]};
         if (cg == 0) {
           float Mr = kNegInf, Lr = 0.f;
 #pragma unroll
@@ -1771,7 +1773,7 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
   const int wpr = p.n_chunks >= 16 ? 4 : 1;  // waves per merged row
   const int n_row_wgs = (p.B * p.Hkv * p.R * wpr + 3) / 4;
   const long long n_s = p.scores ? ((long long)p.B * p.P_max + 255) / 256 : 0;
-  if (p.treek)  // the tree kernel writes its o partials in bf16
+  if (p.treek || p.stream)  // the bf16 kernels write their o partials in bf16
     hipLaunchKernelGGL((verify_merge<T, D, true>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
   else
     hipLaunchKernelGGL((verify_merge<T, D, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
