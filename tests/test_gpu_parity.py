@@ -215,6 +215,26 @@ def _sparse_call_and_check(wl, dw, lists, stride, max_idx, ws, what):
     check_out(as_f64(out), ref, wl.dtype, what)
 
 
+@pytest.mark.parametrize("dtype,D,paged", [("bf16", 128, False), ("bf16", 64, True), ("f32", 128, False)])
+def test_sparse_large_grid_chunks(dtype, D, paged):
+    """Many lists (B * Hkv * ceil(max_idx / 64) >= 1024 workgroups) switch the
+    draft step to 128-position chunks: ragged counts (a partial last chunk, a
+    count below one chunk, zero, the full stride) still match the oracle."""
+    Hkv, B = 8, 8
+    P = [1500, 1300, 900, 700, 1500, 300, 1100, 1250]
+    wl = make_custom(seed=230 + D, B=B, Hq=2 * Hkv, Hkv=Hkv, D=D, dtype=dtype, P=P, N=4, score_rows="all",
+                     k_sel=10, decode_steps=1, q_std_mult=6.0, layout="paged" if paged else "contiguous",
+                     page_size=16)
+    dw = DevWorkload(wl)
+    stride = 1100
+    plan_wgs = B * Hkv * ((stride + 63) // 64)
+    assert plan_wgs >= 1024
+    rng = np.random.default_rng(7)
+    sizes = [1100, 129, 0, 600, 127, 1, 1000, 200]
+    lists = [rng.choice(int(P[b]) + 4, sizes[b], replace=False).astype(np.int32) for b in range(B)]
+    _sparse_call_and_check(wl, dw, lists, stride, stride, sv.Workspace(), f"large grid {dtype} D={D}")
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_sparse_workspace_garbage_and_reuse(paged):
     """The workspace is scratch: a workspace full of garbage, and the same
