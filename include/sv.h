@@ -347,6 +347,28 @@ sv_status sv_validate_index(int B, int lists_per_seq, const sv_kv_cache* kv, con
                             const int32_t* n_idx, int max_idx, int32_t* err, sv_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* Verification attention that allocates nothing, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops and
+ * harnesses that forbid hipMalloc).
+ *
+ * Same arguments and results as sv_verify_attn, without the workspace: the
+ * scratch it needs (chunk partials, score partials, ancestor sets) is a
+ * static device array of SV_NOALLOC_SCRATCH_BYTES owned by the library, one
+ * per GPU, held until the process ends.  A call whose scratch need
+ * (sv_verify_workspace_size of the same arguments) exceeds it returns
+ * SV_E_WORKSPACE and launches nothing.  The array's contents are not needed
+ * on entry.  All calls on one GPU share its array: calls that may overlap on
+ * one GPU (different streams, threads or processes sharing the library
+ * instance) race and give unspecified results; calls ordered on one stream
+ * are safe.  The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress); no call allocates or frees memory. */
+#define SV_NOALLOC_SCRATCH_BYTES (64u << 20)
+sv_status sv_verify_attn_noalloc(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                                 const sv_kv_cache* kv, const int32_t* prefix_len, int P_max,
+                                 const int32_t* parent, const int32_t* score_rows_host, int n_score_rows,
+                                 float softmax_scale, void* out, float* scores, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* Optional timing hook for profiling: while set (non-NULL), every
  * sv_verify_attn call on this thread records `start_event` on its stream right
  * before its main attention kernel and `stop_event` right after it (both are

@@ -20,7 +20,7 @@ EXPORTS = (
     "sv_compact_kv", "sv_dense_draft_workspace_size", "sv_dense_draft_attn", "sv_build_tree",
     "sv_accept_commit",
     "sv_validate_kv", "sv_validate_tree", "sv_validate_index",
-    "sv_set_verify_timing_events",
+    "sv_set_verify_timing_events", "sv_verify_attn_noalloc",
 )
 
 
@@ -96,6 +96,9 @@ def load() -> ctypes.CDLL:
     lib.sv_build_tree.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.sv_accept_commit.restype = i32
     lib.sv_accept_commit.argtypes = [i32, i32, i32, i32, i32, kvp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sv_verify_attn_noalloc.restype = i32
+    lib.sv_verify_attn_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, i32, kvp, vp, i32, vp, vp, i32, f32,
+                                           vp, vp, vp]
     lib.sv_set_verify_timing_events.restype = i32
     lib.sv_set_verify_timing_events.argtypes = [vp, vp]
     _lib = lib

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsv.so")
-SOURCES = ["api.cpp", "verify.hip", "topk.hip", "sparse.hip", "accept.hip", "build_tree.hip", "validate.hip"]
+SOURCES = ["api.cpp", "verify.hip", "topk.hip", "sparse.hip", "accept.hip", "build_tree.hip", "validate.hip", "noalloc.hip"]
 
 
 def hipcc() -> str:

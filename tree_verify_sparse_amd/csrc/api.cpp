@@ -71,6 +71,16 @@ sv_status hip_status(int e, const char* what) {
 
 }  // namespace
 
+namespace sv {
+sv_status set_error(sv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+}  // namespace sv
+
 extern "C" {
 
 int sv_abi_version(void) { return SV_ABI_VERSION; }

@@ -14,6 +14,9 @@ constexpr int kInlineQbarRows = 64;  // scoring (row, head) pairs summed inside 
 constexpr int kQbarPairs = 64;       // pairs per partial sum when a prep kernel forms qbar
 constexpr size_t kAlign = 256;
 
+// Records the thread's error message (sv_last_error) and returns st.
+sv_status set_error(sv_status st, const char* fmt, ...);
+
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
 // How one sv_verify_attn call is split into workgroups and workspace regions.
