@@ -20,6 +20,10 @@ Readings taken where the pages are silent (each also listed in the design notes)
   execution with one-token pages whose page indices are token indices).
 
 Pins (tests/test_oracle_*.py):
+  bf16_bits_to_f64     -- values the bfloat16 format fixes (1.0, -2.5, -0.0, the
+                          largest finite, the smallest normal and subnormal,
+                          infinities); all 65536 patterns == torch's own
+                          bfloat16 -> float64 conversion
   ancestors            -- brute-force reachability, hand-made golden trees
   verify_attention     -- torch SDPA (float64, explicit boolean mask); chain ==
                           separately written triangular mask; golden 2-key case;

@@ -192,8 +192,24 @@ def test_tree_builder_without_sibling_offers_is_caught(monkeypatch):
     assert any(_fails(pins.test_best_first_tree_brute_force, seed) for seed in range(10))
 
 
+def test_bf16_misdecode_is_caught(monkeypatch):
+    # a shift by 15 instead of 16 (an off-by-one in the bit layout), then a
+    # decode that drops the sign bit
+    for bad in (lambda u: (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(15))
+                .view(np.float32).astype(np.float64),
+                lambda u: ((np.asarray(u, dtype=np.uint16).astype(np.uint32) & np.uint32(0x7FFF)) << np.uint32(16))
+                .view(np.float32).astype(np.float64)):
+        _patch(monkeypatch, "bf16_bits_to_f64", bad)
+        assert _fails(pins.test_bf16_decoder_format_values)
+        case = dict(dtype="bf16", B=2, Hq=8, Hkv=2, D=128, P=[200, 333], N=7, tree="best_first", tree_depth=4)
+        assert _fails(pins.test_verify_matches_torch_sdpa, case)
+
+
 def test_unmutated_oracle_passes_the_same_checks():
     # the same check functions pass on the real oracle (guards against vacuous mutation tests)
+    pins.test_bf16_decoder_format_values()
+    pins.test_verify_matches_torch_sdpa(dict(dtype="bf16", B=2, Hq=8, Hkv=2, D=128, P=[200, 333], N=7,
+                                             tree="best_first", tree_depth=4))
     pins.test_golden_attention_three_keys()
     pins.test_golden_tree_uniform()
     pins.test_golden_scores_small()

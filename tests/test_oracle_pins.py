@@ -17,6 +17,36 @@ def f32(x):
     return np.asarray(x, dtype=np.float32)
 
 
+def torch_bf16_to_f64(x):
+    """bfloat16 bit patterns decoded by torch's own bfloat16 type: a decoder
+    independent of the oracle's, for the pins that cross-check it."""
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+# ----------------------------------------------------------------------------- storage format
+
+def test_bf16_decoder_format_values():
+    """bfloat16 = 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits: values
+    the format itself fixes, then every one of the 65536 patterns against torch."""
+    fixed = {
+        0x3F80: 1.0, 0xC020: -2.5, 0x4049: 3.140625, 0x3E80: 0.25, 0x0000: 0.0, 0x8000: -0.0,
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,      # largest finite
+        0x0080: 2.0 ** -126,                         # smallest normal
+        0x0001: 2.0 ** -133,                         # smallest subnormal
+        0x807F: -(127 / 128) * 2.0 ** -126,          # largest negative subnormal
+        0x7F80: np.inf, 0xFF80: -np.inf,
+    }
+    got = oracle.bf16_bits_to_f64(np.array(list(fixed), dtype=np.uint16))
+    for (bits, want), g in zip(fixed.items(), got):
+        assert g == want and np.signbit(g) == np.signbit(want), (hex(bits), g, want)
+    assert np.isnan(oracle.bf16_bits_to_f64(np.array([0x7FC0, 0xFFC1], dtype=np.uint16))).all()
+    every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    a, b = oracle.bf16_bits_to_f64(every), torch_bf16_to_f64(every)
+    nan = np.isnan(b)
+    assert (np.isnan(a) == nan).all()
+    assert np.array_equal(a[~nan], b[~nan]) and (np.signbit(a[~nan]) == np.signbit(b[~nan])).all()
+
+
 # ----------------------------------------------------------------------------- golden
 
 def test_golden_attention_three_keys():
@@ -110,7 +140,7 @@ def _sdpa_verify(wl, b):
     Pb, N, G = int(wl.P[b]), wl.N, wl.Hq // wl.Hkv
     L = Pb + N
     slots = kv.slots(b, np.arange(L))
-    to64 = (lambda x: oracle.bf16_bits_to_f64(x)) if wl.dtype == "bf16" else (lambda x: x.astype(np.float64))
+    to64 = torch_bf16_to_f64 if wl.dtype == "bf16" else (lambda x: x.astype(np.float64))
     K = torch.from_numpy(to64(wl.k[slots])).permute(1, 0, 2)          # [Hkv][L][D]
     V = torch.from_numpy(to64(wl.v[slots])).permute(1, 0, 2)
     K = K.repeat_interleave(G, dim=0)                                 # MHA with repeated K/V
@@ -171,8 +201,8 @@ def test_scores_closed_form(case):
     wl = make_custom(seed=5, **case)
     s = oracle.verify_scores(wl.q, wl.dtype, KVCache.of(wl), wl.P, wl.score_rows, wl.scale, wl.Hkv)
     G = wl.Hq // wl.Hkv
-    q = oracle.bf16_bits_to_f64(wl.q) if wl.dtype == "bf16" else wl.q.astype(np.float64)
-    kall = oracle.bf16_bits_to_f64(wl.k) if wl.dtype == "bf16" else wl.k.astype(np.float64)
+    q = torch_bf16_to_f64(wl.q) if wl.dtype == "bf16" else wl.q.astype(np.float64)
+    kall = torch_bf16_to_f64(wl.k) if wl.dtype == "bf16" else wl.k.astype(np.float64)
     for b in range(wl.B):
         Pb = int(wl.P[b])
         qbar = q[b][wl.score_rows].reshape(len(wl.score_rows), wl.Hkv, G, wl.D).sum(axis=(0, 2))
@@ -238,9 +268,9 @@ def test_sparse_permutation_invariance_and_dense_prefix():
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
     # every prefix position selected == dense decode over the prefix (torch SDPA)
     full = oracle.sparse_draft_attention(wl.dq[0], "bf16", kv, [np.arange(200)], wl.scale, 2)
-    K = torch.from_numpy(oracle.bf16_bits_to_f64(wl.k[:200])).permute(1, 0, 2).repeat_interleave(4, 0)
-    V = torch.from_numpy(oracle.bf16_bits_to_f64(wl.v[:200])).permute(1, 0, 2).repeat_interleave(4, 0)
-    Q = torch.from_numpy(oracle.bf16_bits_to_f64(wl.dq[0, 0]))[:, None, :]
+    K = torch.from_numpy(torch_bf16_to_f64(wl.k[:200])).permute(1, 0, 2).repeat_interleave(4, 0)
+    V = torch.from_numpy(torch_bf16_to_f64(wl.v[:200])).permute(1, 0, 2).repeat_interleave(4, 0)
+    Q = torch.from_numpy(torch_bf16_to_f64(wl.dq[0, 0]))[:, None, :]
     ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=wl.scale)[:, 0].numpy()
     np.testing.assert_allclose(full[0], ref, rtol=1e-10, atol=1e-13)
     # empty index list gives zeros
@@ -389,7 +419,7 @@ def test_dense_draft_single_row_permutation_and_empty():
     one = oracle.dense_draft_attention(wl.dq[0], "bf16", ck, cv, [1, 1], wl.scale, 2)
     for b in range(2):
         for h in range(8):
-            assert np.array_equal(one[b, h], oracle.bf16_bits_to_f64(cv[b, 0, h // 4]))
+            assert np.array_equal(one[b, h], torch_bf16_to_f64(cv[b, 0, h // 4]))
     # rows in another order give the same output
     n = [40, 55]
     base = oracle.dense_draft_attention(wl.dq[0], "bf16", ck, cv, n, wl.scale, 2)
