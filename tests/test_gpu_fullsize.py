@@ -22,7 +22,8 @@ import torch
 import oracle
 from oracle import KVCache as OKV
 from workloads import CONFIG_NAMES, make_workload
-from tests.gpu_util import DevWorkload, as_f64, check_out, check_scores, check_selection_band, i32
+from tests.gpu_util import (DevWorkload, as_f64, attention_abs, check_out, check_out_derived, check_scores,
+                            check_selection_band, i32, score_floor, sparse_abs)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,14 +72,18 @@ def test_full_size_step(cfg):
     rows = _sample_rows(wl, 12, seed=cfg)
     ref = oracle.verify_attention(wl.q, wl.dtype, kv, wl.P, wl.parent, wl.scale, wl.Hkv, rows=rows)
     got = as_f64(out)
+    ab = attention_abs(wl, rows=rows) if wl.dtype == "bf16" else None
     for (b, t, h) in rows:
         check_out(got[b, t, h], ref[b, t, h], wl.dtype, f"verify out (b={b}, t={t}, h={h})")
+        if ab is not None:
+            check_out_derived(got[b, t, h], ref[b, t, h], ab[b, t, h], "verify", f"verify out (b={b}, t={t}, h={h})")
     print(f"  sampled attention rows checked in {time.time() - t0:.1f} s", flush=True)
 
     # every score, and the whole selection
     t0 = time.time()
     ref_s = oracle.verify_scores_grouped(wl.q, wl.dtype, kv, wl.P, wl.score_rows, wl.scale, wl.Hkv, wl.P_max)
-    check_scores(as_f64(scores), ref_s, wl.P)
+    worst, by_floor = check_scores(as_f64(scores), ref_s, wl.P, score_floor(wl))
+    print(f"  scores: worst relative error {worst:.2e}, {by_floor} entries within the fp32 floor only", flush=True)
     ref_idx = [oracle.topk_select(ref_s[b], int(wl.P[b]), int(wl.k_sel[b])) for b in range(wl.B)]
     assert (count.cpu().numpy() == np.minimum(wl.k_sel, wl.P)).all()
     swaps = check_selection_band(idx.cpu().numpy(), ref_s, ref_idx, wl.P, wl.k_sel)
@@ -98,9 +103,14 @@ def test_full_size_step(cfg):
         d = sv.sparse_draft_attn(dw.dq[s], dw.kv, i32(oi), i32(n), max_idx=max(1, wl.k_max))
         dref = oracle.sparse_draft_attention(wl.dq[s], wl.dtype, kv, ref_idx, wl.scale, wl.Hkv)
         check_out(as_f64(d), dref, wl.dtype, f"draft step {s}")
+        dab = sparse_abs(wl, wl.dq[s], ref_idx) if wl.dtype == "bf16" else None
+        if dab is not None:
+            check_out_derived(as_f64(d), dref, dab, "sparse", f"draft step {s}")
         if compact:
             dd = sv.dense_draft_attn(dw.dq[s], ck, cv, i32(n))
             check_out(as_f64(dd), dref, wl.dtype, f"compacted draft step {s}")
+            if dab is not None:
+                check_out_derived(as_f64(dd), dref, dab, "verify", f"compacted draft step {s}")
 
 
 @pytest.mark.parametrize("cfg", [2, 4])

@@ -8,7 +8,8 @@ import torch
 import oracle
 from oracle import KVCache as OKV
 from workloads import make_custom, make_score_vector, make_workload
-from tests.gpu_util import (DevWorkload, as_f64, check_out, check_scores, check_selection_band, i32, to_torch)
+from tests.gpu_util import (DevWorkload, as_f64, attention_abs, check_out, check_out_derived, check_scores,
+                            check_selection_band, i32, score_floor, sparse_abs, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +67,33 @@ CASES = {
     "tree64_stream_mha": lambda: make_custom(
         seed=115, B=1, Hq=4, Hkv=4, D=128, dtype="bf16", P=1900, N=64, tree="best_first", tree_depth=6,
         score_rows="all", k_sel=120),
+    # mask canaries at full tree width: ancestor-set words 2..7 (nodes >= 64), a
+    # prefix over three 2048-key tree chunks, sharpened queries, distinct large V
+    # rows on the verify tokens (a one-key leak moves outputs far past the bound)
+    "tree256_canary": lambda: make_custom(
+        seed=116, B=1, Hq=32, Hkv=8, D=128, dtype="bf16", P=5000, N=256, tree="best_first", tree_depth=8,
+        score_rows="all", k_sel=200, decode_steps=0, q_std_mult=4.0, v_canary=32.0),
+    "paged_tree64_canary": lambda: make_custom(
+        seed=117, B=3, Hq=32, Hkv=8, D=128, dtype="bf16", P=[3000, 900, 4500], N=64, tree="best_first",
+        tree_depth=6, score_rows="all", k_sel="5pct", layout="paged", page_size=16, q_std_mult=4.0,
+        v_canary=32.0),
+    # page sizes other than 16: one token per page, and a size that is not a
+    # power of two (the division path), on the streaming and the tree kernels
+    "chain8_paged_ps1": lambda: make_custom(
+        seed=118, B=2, Hq=32, Hkv=8, D=128, dtype="bf16", P=[2500, 700], N=8, score_rows="c2q", k_sel=100,
+        layout="paged", page_size=1, q_std_mult=4.0),
+    "chain8_paged_ps24": lambda: make_custom(
+        seed=119, B=2, Hq=32, Hkv=8, D=128, dtype="bf16", P=[2500, 701], N=8, score_rows="c2q", k_sel=100,
+        layout="paged", page_size=24, q_std_mult=4.0),
+    "tree64_paged_ps1": lambda: make_custom(
+        seed=120, B=2, Hq=32, Hkv=8, D=128, dtype="bf16", P=[2100, 333], N=64, tree="best_first", tree_depth=6,
+        score_rows="all", k_sel=64, layout="paged", page_size=1, q_std_mult=4.0, v_canary=8.0),
+    "tree64_paged_ps24": lambda: make_custom(
+        seed=121, B=2, Hq=32, Hkv=8, D=128, dtype="bf16", P=[2100, 333], N=64, tree="best_first", tree_depth=6,
+        score_rows="all", k_sel=64, layout="paged", page_size=24, q_std_mult=4.0, v_canary=8.0),
+    "f32_chain_paged_ps24": lambda: make_custom(
+        seed=122, B=2, Hq=8, Hkv=2, D=64, dtype="f32", P=[900, 250], N=5, score_rows="all", k_sel=40,
+        layout="paged", page_size=24, q_std_mult=4.0),
 }
 
 
@@ -89,10 +117,13 @@ def test_verify_and_step_parity(name):
     out, scores = dw.verify()
     torch.cuda.synchronize()
     check_out(as_f64(out), ref["out"], wl.dtype, "verify out")
+    if wl.dtype == "bf16":
+        check_out_derived(as_f64(out), ref["out"], attention_abs(wl), "verify", "verify out")
     if not len(wl.score_rows):
         assert scores is None
         return
-    check_scores(as_f64(scores), ref["scores"], wl.P)
+    worst, by_floor = check_scores(as_f64(scores), ref["scores"], wl.P, score_floor(wl))
+    print(f"  scores: worst relative error {worst:.2e}, {by_floor} entries within the fp32 floor only", flush=True)
     idx, count = sv.topk_select(scores, dw.P, dw.k_sel, wl.k_max)
     gi = idx.cpu().numpy()
     kk = np.minimum(wl.k_sel, wl.P)
@@ -107,9 +138,32 @@ def test_verify_and_step_parity(name):
         d = sv.sparse_draft_attn(dw.dq[s], dw.kv, i32(oi), i32(n), max_idx=max(1, wl.k_max))
         dref = oracle.sparse_draft_attention(wl.dq[s], wl.dtype, OKV.of(wl), ref["idx"], wl.scale, wl.Hkv)
         check_out(as_f64(d), dref, wl.dtype, f"draft step {s}")
+        if wl.dtype == "bf16":
+            check_out_derived(as_f64(d), dref, sparse_abs(wl, wl.dq[s], ref["idx"]), "sparse", f"draft step {s}")
 
 
-@pytest.mark.parametrize("name", ["batch4_chain16", "tree256_bf16", "paged5_tree64"])
+def test_page_table_longer_than_the_cached_slice():
+    """One token per page and over a million positions: a verify chunk spans
+    more pages than its LDS copy of the page table holds, and the pages past
+    it are read from memory.  Sampled rows against the oracle, every score."""
+    print("[case] paged ps=1, P=1050000", flush=True)
+    wl = make_custom(seed=130, B=1, Hq=4, Hkv=1, D=64, dtype="bf16", P=1_050_000, N=4, score_rows="all",
+                     k_sel=64, decode_steps=0, layout="paged", page_size=1, q_std_mult=4.0)
+    dw = DevWorkload(wl)
+    out, scores = dw.verify()
+    torch.cuda.synchronize()
+    rows = [(0, t, h) for t in (0, 3) for h in range(4)]
+    ref = oracle.verify_attention(wl.q, wl.dtype, OKV.of(wl), wl.P, None, wl.scale, wl.Hkv, rows=rows)
+    got = as_f64(out)
+    ab = attention_abs(wl, rows=rows)
+    for (b, t, h) in rows:
+        check_out(got[b, t, h], ref[b, t, h], "bf16", f"verify out t={t} h={h}")
+        check_out_derived(got[b, t, h], ref[b, t, h], ab[b, t, h], "verify", f"verify out t={t} h={h}")
+    ref_s = oracle.verify_scores_grouped(wl.q, wl.dtype, OKV.of(wl), wl.P, wl.score_rows, wl.scale, wl.Hkv, wl.P_max)
+    check_scores(as_f64(scores), ref_s, wl.P, score_floor(wl))
+
+
+@pytest.mark.parametrize("name", ["batch4_chain16", "tree256_bf16", "paged5_tree64", "tree256_canary"])
 def test_verify_is_deterministic(name):
     """No float atomics anywhere: reruns are bit-identical (scores compared where written, i < P_b)."""
     wl = CASES[name]()
@@ -169,13 +223,13 @@ def test_topk_degenerate():
 
 # --------------------------------------------------------------------------- sparse draft, direct
 
-@pytest.mark.parametrize("dtype,D,G,paged", [("bf16", 128, 4, False), ("bf16", 64, 2, True),
-                                             ("f32", 128, 4, True), ("f32", 64, 1, False)])
-def test_sparse_draft_direct(dtype, D, G, paged):
+@pytest.mark.parametrize("dtype,D,G,ps", [("bf16", 128, 4, 0), ("bf16", 64, 2, 16), ("f32", 128, 4, 16),
+                                          ("f32", 64, 1, 0), ("bf16", 128, 4, 24), ("bf16", 128, 2, 1)])
+def test_sparse_draft_direct(dtype, D, G, ps):
     Hkv = 4
-    wl = make_custom(seed=200 + D + G, B=3, Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype, P=[700, 64, 300], N=4,
+    wl = make_custom(seed=200 + D + G + ps, B=3, Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype, P=[700, 64, 300], N=4,
                      score_rows="all", k_sel=10, decode_steps=2, q_std_mult=6.0,
-                     layout="paged" if paged else "contiguous", page_size=16)
+                     layout="paged" if ps else "contiguous", page_size=ps or 16)
     dw = DevWorkload(wl)
     rng = np.random.default_rng(D + G)
     lists = [rng.choice(704, 257, replace=False),                       # spans prefix and verify tokens
@@ -190,6 +244,8 @@ def test_sparse_draft_direct(dtype, D, G, paged):
     ref = oracle.sparse_draft_attention(wl.dq[1], dtype, OKV.of(wl), lists, wl.scale, wl.Hkv)
     g = as_f64(out)
     check_out(g, ref, dtype, "sparse draft")
+    if dtype == "bf16":
+        check_out_derived(g, ref, sparse_abs(wl, wl.dq[1], lists), "sparse", "sparse draft")
     assert (g[1] == 0).all()
 
 

@@ -9,7 +9,7 @@ import torch
 import oracle
 from oracle import KVCache as OKV
 from workloads import make_custom
-from tests.gpu_util import DevWorkload, as_f64, check_out, check_scores, check_selection_band, i32
+from tests.gpu_util import DevWorkload, as_f64, check_out, check_scores, check_selection_band, i32, score_floor
 
 pytestmark = pytest.mark.gpu
 
@@ -46,11 +46,13 @@ def test_per_head_scores_selection_and_draft(name):
     g = as_f64(hs)
     B, H = wl.B, wl.Hkv
     P_rows = np.repeat(wl.P, H)
-    check_scores(g.reshape(B * H, -1), ref.reshape(B * H, -1), P_rows)
-    # the attention output is that of the ordinary call
+    floor_h = score_floor(wl, rows=rows, per_head=True)
+    check_scores(g.reshape(B * H, -1), ref.reshape(B * H, -1), P_rows, floor_h.reshape(B * H, -1))
+    # the attention output is that of the ordinary call, and the per-head scores
+    # sum to its scores (the merge's fp32 sum over the heads: the same floor)
     out2, tot = dw.verify()
     assert torch.equal(out, out2)
-    check_scores(g.sum(axis=1), as_f64(tot).astype(np.float64), wl.P)
+    check_scores(g.sum(axis=1), as_f64(tot).astype(np.float64), wl.P, score_floor(wl, rows=rows))
     # top-k per (sequence, KV head): the B * Hkv rows through the ordinary selection
     k_rows = np.repeat(wl.k_sel, H)
     idx, count = sv.topk_select(hs.view(B * H, wl.P_max), i32(P_rows), i32(k_rows), wl.k_max)

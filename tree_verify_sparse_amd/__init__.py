@@ -28,7 +28,7 @@ __all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_a
            "dense_draft_attn", "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size",
            "dense_draft_workspace_size", "build_tree", "accept_commit", "verify_attn_per_head",
            "sparse_draft_attn_per_head", "select_sink_window", "timing_events", "SvError", "lib",
-           "validate_kv", "validate_tree", "validate_index", "ContractError"]
+           "validate_kv", "validate_tree", "validate_index", "ContractError", "verify_attn_noalloc"]
 
 
 def lib() -> ctypes.CDLL:
@@ -55,6 +55,48 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Argument checks.  The C ABI sees only pointers and sizes, so tensors that
+# disagree with each other (a float32 query with a bfloat16 cache, a head dim
+# other than the cache's, an output or index buffer of the wrong shape) would
+# make the kernels read or write past an allocation.  Every entry point below
+# checks its tensors against each other first, before any pointer is taken or
+# anything is launched, and raises ValueError.
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_i32(t: Optional[torch.Tensor], shape: tuple, name: str, dev) -> None:
+    if t is None:
+        return
+    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _need(t.device == dev, f"{name} is on {t.device}, the call runs on {dev}")
+
+
+def _check_like(t: Optional[torch.Tensor], shape: tuple, dtype, name: str, dev) -> None:
+    if t is None:
+        return
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _need(t.device == dev, f"{name} is on {t.device}, the call runs on {dev}")
+
+
+def _check_kv(kv: "KVCache", dtype, D: int, Hq: int, dev) -> None:
+    _need(kv.k.dim() == 3 and tuple(kv.k.shape) == tuple(kv.v.shape), "kv.k and kv.v must both be [num_slots][Hkv][D]")
+    _need(kv.k.dtype == kv.v.dtype, f"kv.k ({kv.k.dtype}) and kv.v ({kv.v.dtype}) must share a dtype")
+    _need(kv.k.dtype == dtype, f"query dtype {dtype} differs from the KV cache's {kv.k.dtype}")
+    _need(kv.D == D, f"query head dim {D} differs from the KV cache's {kv.D}")
+    _need(Hq % kv.Hkv == 0, f"{Hq} query heads are not a multiple of the cache's {kv.Hkv} KV heads")
+    _need(kv.k.device == dev and kv.v.device == dev, f"the KV cache is on {kv.k.device}, the call runs on {dev}")
+    if kv.page_table is not None:
+        pt = kv.page_table
+        _need(pt.dtype == torch.int32 and pt.dim() == 2, "kv.page_table must be int32 [B][max_pages]")
+        _need(pt.device == dev, f"kv.page_table is on {pt.device}, the call runs on {dev}")
 
 
 @dataclasses.dataclass
@@ -131,8 +173,15 @@ def verify_attn(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max
     ``score_rows``: verify nodes whose logits are summed into the scores
     (None or [] = no scores).  ``parent``: int32 [B][N] draft tree or None (chain).
     """
-    L = lib()
+    _need(q.dim() == 4, "q must be [B][N][Hq][D]")
     B, N, Hq, D = (int(x) for x in q.shape)
+    dev = q.device
+    _check_kv(kv, q.dtype, D, Hq, dev)
+    _check_i32(prefix_len, (B,), "prefix_len", dev)
+    _check_i32(parent, (B, N), "parent", dev)
+    _check_like(out, tuple(q.shape), q.dtype, "out", dev)
+    _check_like(scores, (B, int(P_max)), torch.float32, "scores", dev)
+    L = lib()
     rows = [int(r) for r in (score_rows or [])]
     if out is None:
         out = torch.empty_like(q)
@@ -154,6 +203,34 @@ def verify_attn(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max
     return out, (scores if rows else None)
 
 
+def verify_attn_noalloc(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, *, P_max: int,
+                        parent: Optional[torch.Tensor] = None, score_rows: Optional[Sequence[int]] = None,
+                        scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                        scores: Optional[torch.Tensor] = None):
+    """sv_verify_attn_noalloc: verify_attn on the library's static scratch (no
+    workspace; the caller still passes or gets out and scores)."""
+    _need(q.dim() == 4, "q must be [B][N][Hq][D]")
+    B, N, Hq, D = (int(x) for x in q.shape)
+    dev = q.device
+    _check_kv(kv, q.dtype, D, Hq, dev)
+    _check_i32(prefix_len, (B,), "prefix_len", dev)
+    _check_i32(parent, (B, N), "parent", dev)
+    _check_like(out, tuple(q.shape), q.dtype, "out", dev)
+    _check_like(scores, (B, int(P_max)), torch.float32, "scores", dev)
+    L = lib()
+    rows = [int(r) for r in (score_rows or [])]
+    if out is None:
+        out = torch.empty_like(q)
+    if rows and scores is None:
+        scores = torch.empty((B, P_max), dtype=torch.float32, device=dev)
+    rows_arr = (ctypes.c_int32 * max(1, len(rows)))(*rows)
+    kvs = kv.c_struct()
+    _lib.check(L.sv_verify_attn_noalloc(_ptr(q), _dtype_code(q), B, N, Hq, kv.Hkv, D, ctypes.byref(kvs),
+                                        _ptr(prefix_len), P_max, _ptr(parent), rows_arr, len(rows), float(scale),
+                                        _ptr(out), _ptr(scores) if rows else None, _stream(dev)))
+    return out, (scores if rows else None)
+
+
 def topk_workspace_size(B, P_max) -> int:
     return int(lib().sv_topk_workspace_size(B, P_max))
 
@@ -162,8 +239,14 @@ def topk_select(scores: torch.Tensor, prefix_len: torch.Tensor, k: torch.Tensor,
                 idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
                 workspace: Optional[Workspace] = None):
     """sv_topk_select: -> (idx int32 [B][k_max] ascending, -1 padded; count int32 [B])."""
-    L = lib()
+    _need(scores.dim() == 2 and scores.dtype == torch.float32, "scores must be float32 [B][P_max]")
     B, P_max = (int(x) for x in scores.shape)
+    dev = scores.device
+    _check_i32(prefix_len, (B,), "prefix_len", dev)
+    _check_i32(k, (B,), "k", dev)
+    _check_i32(idx, (B, int(k_max)), "idx", dev)
+    _check_i32(count, (B,), "count", dev)
+    L = lib()
     if idx is None:
         idx = torch.empty((B, k_max), dtype=torch.int32, device=scores.device)
     if count is None:
@@ -178,10 +261,18 @@ def sparse_draft_attn(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, n_idx: to
                       max_idx: Optional[int] = None, scale: float = 0.0, out: Optional[torch.Tensor] = None,
                       workspace: Optional[Workspace] = None):
     """sv_sparse_draft_attn: q [B][Hq][D], idx int32 [B][stride] logical positions, n_idx int32 [B]."""
-    L = lib()
+    _need(q.dim() == 3, "q must be [B][Hq][D]")
     B, Hq, D = (int(x) for x in q.shape)
+    dev = q.device
+    _check_kv(kv, q.dtype, D, Hq, dev)
+    _need(idx.dim() == 2 and int(idx.shape[0]) == B, "idx must be int32 [B][stride]")
     stride = int(idx.shape[1])
+    _check_i32(idx, (B, stride), "idx", dev)
+    _check_i32(n_idx, (B,), "n_idx", dev)
+    _check_like(out, tuple(q.shape), q.dtype, "out", dev)
     max_idx = stride if max_idx is None else int(max_idx)
+    _need(0 <= max_idx <= stride, f"max_idx = {max_idx} must lie in [0, {stride}]")
+    L = lib()
     if out is None:
         out = torch.empty_like(q)
     dt = _dtype_code(q)
@@ -201,8 +292,15 @@ def verify_attn_per_head(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor,
                          scale: float = 0.0, out: Optional[torch.Tensor] = None,
                          head_scores: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
     """sv_verify_attn_per_head: -> (out [B][N][Hq][D], head_scores fp32 [B][Hkv][P_max])."""
-    L = lib()
+    _need(q.dim() == 4, "q must be [B][N][Hq][D]")
     B, N, Hq, D = (int(x) for x in q.shape)
+    dev = q.device
+    _check_kv(kv, q.dtype, D, Hq, dev)
+    _check_i32(prefix_len, (B,), "prefix_len", dev)
+    _check_i32(parent, (B, N), "parent", dev)
+    _check_like(out, tuple(q.shape), q.dtype, "out", dev)
+    _check_like(head_scores, (B, kv.Hkv, int(P_max)), torch.float32, "head_scores", dev)
+    L = lib()
     rows = [int(r) for r in score_rows]
     if out is None:
         out = torch.empty_like(q)
@@ -224,10 +322,18 @@ def sparse_draft_attn_per_head(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, 
                                max_idx: Optional[int] = None, scale: float = 0.0,
                                out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
     """sv_sparse_draft_attn_per_head: idx int32 [B][Hkv][stride], n_idx int32 [B][Hkv]."""
-    L = lib()
+    _need(q.dim() == 3, "q must be [B][Hq][D]")
     B, Hq, D = (int(x) for x in q.shape)
+    dev = q.device
+    _check_kv(kv, q.dtype, D, Hq, dev)
+    _need(idx.dim() == 3 and tuple(idx.shape[:2]) == (B, kv.Hkv), "idx must be int32 [B][Hkv][stride]")
     stride = int(idx.shape[2])
+    _check_i32(idx, (B, kv.Hkv, stride), "idx", dev)
+    _check_i32(n_idx, (B, kv.Hkv), "n_idx", dev)
+    _check_like(out, tuple(q.shape), q.dtype, "out", dev)
     max_idx = stride if max_idx is None else int(max_idx)
+    _need(0 <= max_idx <= stride, f"max_idx = {max_idx} must lie in [0, {stride}]")
+    L = lib()
     if out is None:
         out = torch.empty_like(q)
     dt = _dtype_code(q)
@@ -243,8 +349,10 @@ def sparse_draft_attn_per_head(q: torch.Tensor, kv: KVCache, idx: torch.Tensor, 
 
 def select_sink_window(prefix_len: torch.Tensor, P_max: int, sink: int, window: int, k_max: int):
     """sv_select_sink_window: -> (idx int32 [B][k_max], count int32 [B])."""
-    L = lib()
+    _need(prefix_len.dim() == 1, "prefix_len must be int32 [B]")
     B = int(prefix_len.shape[0])
+    _check_i32(prefix_len, (B,), "prefix_len", prefix_len.device)
+    L = lib()
     idx = torch.empty((B, k_max), dtype=torch.int32, device=prefix_len.device)
     count = torch.empty((B,), dtype=torch.int32, device=prefix_len.device)
     _lib.check(L.sv_select_sink_window(B, int(P_max), _ptr(prefix_len), int(sink), int(window), int(k_max), _ptr(idx),
@@ -256,11 +364,18 @@ def compact_kv(kv: KVCache, idx: torch.Tensor, n_idx: torch.Tensor, cap: int, *,
                ck: Optional[torch.Tensor] = None, cv: Optional[torch.Tensor] = None):
     """sv_compact_kv: the listed rows gathered into dense ck, cv [B][cap][Hkv][D]
     (rows past n_idx[b] are left as they were; new buffers start zeroed)."""
-    L = lib()
-    B = int(idx.shape[0])
-    stride = int(idx.shape[1])
+    _need(idx.dim() == 2, "idx must be int32 [B][stride]")
+    B, stride = int(idx.shape[0]), int(idx.shape[1])
+    dev = kv.k.device
+    _check_kv(kv, kv.k.dtype, kv.D, kv.Hkv, dev)
+    _check_i32(idx, (B, stride), "idx", dev)
+    _check_i32(n_idx, (B,), "n_idx", dev)
     max_idx = stride if max_idx is None else int(max_idx)
+    _need(0 <= max_idx <= stride, f"max_idx = {max_idx} must lie in [0, {stride}]")
     shape = (B, cap, kv.Hkv, kv.D)
+    _check_like(ck, shape, kv.k.dtype, "ck", dev)
+    _check_like(cv, shape, kv.k.dtype, "cv", dev)
+    L = lib()
     if ck is None:
         ck = torch.zeros(shape, dtype=kv.k.dtype, device=kv.k.device)
     if cv is None:
@@ -281,11 +396,18 @@ def dense_draft_attn(q: torch.Tensor, ck: torch.Tensor, cv: torch.Tensor, n_rows
                      scale: float = 0.0, out: Optional[torch.Tensor] = None,
                      workspace: Optional[Workspace] = None):
     """sv_dense_draft_attn: q [B][Hq][D] over rows [0, n_rows[b]) of ck, cv [B][cap][Hkv][D]."""
-    L = lib()
+    _need(q.dim() == 3, "q must be [B][Hq][D]")
     B, Hq, D = (int(x) for x in q.shape)
     if ck.dim() != 4 or ck.shape != cv.shape or int(ck.shape[0]) != B or int(ck.shape[3]) != D:
         raise ValueError("ck and cv must both be [B][cap][Hkv][D]")
     cap, Hkv = int(ck.shape[1]), int(ck.shape[2])
+    dev = q.device
+    _need(ck.dtype == q.dtype and cv.dtype == q.dtype, f"ck / cv ({ck.dtype}, {cv.dtype}) must have q's dtype {q.dtype}")
+    _need(Hq % Hkv == 0, f"{Hq} query heads are not a multiple of {Hkv} KV heads")
+    _need(ck.device == dev and cv.device == dev, "ck and cv must be on q's device")
+    _check_i32(n_rows, (B,), "n_rows", dev)
+    _check_like(out, tuple(q.shape), q.dtype, "out", dev)
+    L = lib()
     if out is None:
         out = torch.empty_like(q)
     dt = _dtype_code(q)
@@ -316,9 +438,16 @@ def accept_commit(draft_tokens: torch.Tensor, target_tokens: torch.Tensor, *, pa
     """sv_accept_commit: greedy acceptance (and, with kv, the accepted branch's
     K/V moved in place behind the prefix).  Returns (path int32 [B][N],
     n_accepted int32 [B], bonus int32 [B], new_prefix_len int32 [B] or None)."""
-    L = lib()
+    _need(draft_tokens.dim() == 2, "draft_tokens must be int32 [B][N]")
     B, N = (int(x) for x in draft_tokens.shape)
     dev = draft_tokens.device
+    _check_i32(draft_tokens, (B, N), "draft_tokens", dev)
+    _check_i32(target_tokens, (B, N), "target_tokens", dev)
+    _check_i32(parent, (B, N), "parent", dev)
+    _check_i32(prefix_len, (B,), "prefix_len", dev)
+    if kv is not None:
+        _check_kv(kv, kv.k.dtype, kv.D, kv.Hkv, dev)
+    L = lib()
     path = torch.empty((B, N), dtype=torch.int32, device=dev)
     n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
     bonus = torch.empty((B,), dtype=torch.int32, device=dev)

@@ -194,7 +194,10 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
     long long s;
     if constexpr (PAGED) {
       const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
-      const int e = pt_lds[pg - pg0];  // the plan keeps every chunk within PT_CAP pages
+      // pages past the cached slice (a chunk longer than PT_CAP pages) are read from memory
+      const int jp = pg - pg0;
+      const int e = jp < RG::PT_CAP ? pt_lds[jp]
+                                : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
       s = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
     } else {
       s = seq_base + pos;
@@ -723,7 +726,10 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
     long long sl;
     if constexpr (PAGED) {
       const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
-      const int e = pt_lds[pg - pg0];  // the plan keeps every chunk within PT_CAP pages
+      // pages past the cached slice (a chunk longer than PT_CAP pages) are read from memory
+      const int jp = pg - pg0;
+      const int e = jp < WRg::PT_CAP ? pt_lds[jp]
+                                : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
       sl = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
     } else {
       sl = seq_base + pos;
@@ -1146,7 +1152,10 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
     long long sl;
     if constexpr (PAGED) {
       const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
-      const int e = pt_lds[pg - pg0];  // the plan keeps every chunk within PT_CAP pages
+      // pages past the cached slice (a chunk longer than PT_CAP pages) are read from memory
+      const int jp = pg - pg0;
+      const int e = jp < RG::PT_CAP ? pt_lds[jp]
+                                : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
       sl = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
     } else {
       sl = seq_base + pos;
@@ -1640,7 +1649,7 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
     long long want = (256 + units / 2) / units;
     if (want < 1) want = 1;
     if (want > (nbk + 3) / 4) want = (nbk + 3) / 4;  // at least one block per wave on average
-    if (page_size > 0) {  // a chunk's page-table slice must fit the LDS copy (PT_CAP entries)
+    if (page_size > 0) {  // a chunk's page-table slice should fit the LDS copy (PT_CAP entries; pages past it are read from memory)
       const long long cap_blocks = ((long long)(WaveRing<128>::PT_CAP - 2) * page_size) / 32 - 1;
       const long long need = (nbk + cap_blocks - 1) / (cap_blocks > 0 ? cap_blocks : 1);
       if (want < need) want = need;
@@ -1687,7 +1696,7 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
     if (nc < (nst + max_st - 1) / max_st) nc = (nst + max_st - 1) / max_st;
     if (nc > nst) nc = nst;
     if (nc < 1) nc = 1;
-    if (page_size > 0) {  // a chunk's page-table slice must fit the LDS copy (Ring::PT_CAP entries)
+    if (page_size > 0) {  // a chunk's page-table slice should fit the LDS copy (Ring::PT_CAP entries; pages past it are read from memory)
       const long long cap_st = (long long)(Ring<float, 64>::PT_CAP - 2) * page_size / SK - 1;
       const long long need = (nst + (cap_st > 0 ? cap_st : 1) - 1) / (cap_st > 0 ? cap_st : 1);
       if (nc < need) nc = need;
