@@ -57,6 +57,9 @@ def parse():
                     help="scores: one key set per sequence from the fused scores (the method); per_head: one "
                          "set per KV head from per-head scores; sink_window: the first 64 and the last k - 64 "
                          "positions, no scores (the query-agnostic baseline)")
+    ap.add_argument("--select-path", choices=["fused", "separate"], default="fused",
+                    help="fused: sv_verify_select (the selection inside the verification's last kernel); "
+                         "separate: sv_verify_attn then sv_topk_select (same results)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
@@ -140,6 +143,15 @@ def main():
               for s in range(n_draft)] for kv in kvs]
     f_verify, f_topk, f_sparse, f_hook = L.sv_verify_attn, L.sv_topk_select, L.sv_sparse_draft_attn, \
         L.sv_set_verify_timing_events
+    # fused verification + selection: one call, one workspace holding both
+    fused = args.select_path == "fused" and args.selection == "scores" and rows and wl.P_max <= 131072
+    if fused:
+        fws_n = sv.verify_select_workspace_size(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, wl.P_max, dt, parent is not None,
+                                                len(rows), wl.page_size if pt is not None else 0)
+        fws = torch.empty(max(1, fws_n), dtype=torch.uint8, device=dev)
+        fargs = [a[:14] + (ksel.data_ptr(), kmax, out.data_ptr(), scores.data_ptr(), idx.data_ptr(),
+                           count.data_ptr(), fws.data_ptr(), fws_n, sp) for a in vargs]
+    f_fused = L.sv_verify_select
     # compacted draft loop: the selected rows gathered once per step into dense
     # [B][k_max][Hkv][D] buffers, every draft step decoding over rows [0, count)
     draft_path = args.draft_path
@@ -185,8 +197,11 @@ def main():
         c = i % copies
         if ev is not None:
             f_hook(ev[0].cuda_event, ev[1].cuda_event)
-        st = f_verify(*vargs[c])
-        st |= f_topk(*targs)
+        if fused:
+            st = f_fused(*fargs[c])
+        else:
+            st = f_verify(*vargs[c])
+            st |= f_topk(*targs)
         if draft_path == "compact" and n_draft > 0:
             st |= f_compact(*cargs[c])
             for a in ddargs:
@@ -375,7 +390,7 @@ def main():
 
         def target(i):
             c = i % copies
-            st = f_verify(*vargs[c]) | f_topk(*targs)
+            st = f_fused(*fargs[c]) if fused else (f_verify(*vargs[c]) | f_topk(*targs))
             if draft_path == "compact":
                 st |= f_compact(*cargs[c])
             if st:
@@ -401,6 +416,7 @@ def main():
                    "prefix": int(wl.P_max) if wl.B == 1 else [int(x) for x in wl.P], "verify_nodes": wl.N,
                    "tree": wl.parent is not None, "score_rows": len(rows), "k": int(wl.k_sel.max()),
                    "draft_steps": n_draft, "draft_path": draft_path, "selection": selection,
+                   "select_path": "fused" if fused else "separate",
                    "paged": wl.layout == "paged",
                    "kv_copies_rotated": copies,
                    "step_bytes": step_bytes, "parallelism": "single-gpu"},

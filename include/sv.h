@@ -151,15 +151,46 @@ sv_status sv_verify_attn(const void* q, sv_dtype dtype, int B, int N, int Hq, in
  *   k_max        host scalar: row stride of idx.
  *   idx          device int32[B][k_max]: the k'_b selected indices in increasing
  *                order, then -1 up to k_max.  Ties are broken toward the lower
- *                index; -0.0 and +0.0 are equal.  Scores must be finite.
- *   count        device int32[B] (may be NULL): k'_b.
- *   workspace    sv_topk_workspace_size(B, P_max) bytes of device scratch (currently
- *                0: NULL is accepted); contents on entry are ignored.
+ *                index; -0.0 and +0.0 are equal.  Scores must be finite; NaN
+ *                entries are never selected (unless k'_b = P_b), so a row with
+ *                fewer than k'_b others gets fewer indices.
+ *   count        device int32[B] (may be NULL): the number of indices written
+ *                (k'_b for finite scores).
+ *   workspace    sv_topk_workspace_size(B, P_max) bytes of device scratch;
+ *                contents on entry are ignored.
  */
 size_t sv_topk_workspace_size(int B, int P_max);
 sv_status sv_topk_select(const float* scores, int B, int P_max, const int32_t* prefix_len,
                          const int32_t* k, int k_max, int32_t* idx, int32_t* count,
                          void* workspace, size_t workspace_bytes, sv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Verification with the selection fused in (Vegas §2 steps 1-2: the critical
+ * entries are selected as a by-product of the verification pass).  Exactly
+ * sv_verify_attn followed by sv_topk_select on its scores (same outputs,
+ * bit for bit), with the selection's first pass run on the scores as they are
+ * summed and its second pass on the last workgroup of each sequence to finish,
+ * inside the verification's final kernel, so no launch and no trip through
+ * memory is spent between the two.
+ *
+ *   Arguments as sv_verify_attn, plus (as sv_topk_select):
+ *   k            device int32[B]: requested k_b; k'_b = min(k_b, P_b, k_max).
+ *   k_max        host scalar: row stride of idx.
+ *   idx          device int32[B][k_max]: selected prefix indices, increasing,
+ *                then -1.
+ *   count        device int32[B] (may be NULL): the number of indices written.
+ *   n_score_rows must be >= 1 and P_max <= 131072 (SV_E_UNSUPPORTED above:
+ *   use the two calls).
+ *   workspace    sv_verify_select_workspace_size(...) bytes (same arguments
+ *                as sv_verify_workspace_size); contents on entry are ignored.
+ */
+size_t sv_verify_select_workspace_size(int B, int N, int Hq, int Hkv, int D, int P_max, sv_dtype dtype,
+                                       int is_tree, int n_score_rows, int page_size);
+sv_status sv_verify_select(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                           const sv_kv_cache* kv, const int32_t* prefix_len, int P_max, const int32_t* parent,
+                           const int32_t* score_rows_host, int n_score_rows, float softmax_scale,
+                           const int32_t* k, int k_max, void* out, float* scores, int32_t* idx, int32_t* count,
+                           void* workspace, size_t workspace_bytes, sv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* Sparse draft attention (Vegas §2 step 3 and §3: decode attention of one

@@ -100,7 +100,30 @@ def test_workspace_sizes_are_consistent():
     p16 = lib.sv_verify_workspace_size(2, 8, 32, 8, 128, 65536, _lib.SV_BF16, 0, 2, 16)
     assert p1 > p16 > 0
     assert lib.sv_sparse_workspace_size(1, 32, 8, 128, 2048) >= 32 * 32 * 128 * 4
-    assert lib.sv_topk_workspace_size(4, 131072) == 0          # selection keeps its state on chip
+    # selection: per row, 32 blocks of 512 candidate slots (value and index)
+    assert lib.sv_topk_workspace_size(4, 131072) >= 4 * 32 * 512 * 8
+    fused = lib.sv_verify_select_workspace_size(1, 8, 32, 8, 128, 32768, _lib.SV_BF16, 0, 2, 0)
+    assert fused >= chain + lib.sv_topk_workspace_size(1, 32768)
+    assert lib.sv_verify_select_workspace_size(1, 8, 32, 8, 128, 32768, _lib.SV_BF16, 0, 0, 0) == 0  # no scores
+    assert lib.sv_verify_select_workspace_size(1, 8, 32, 8, 128, 131073, _lib.SV_BF16, 0, 2, 0) == 0  # too long
+
+
+def test_verify_select_rejects_bad_arguments():
+    lib = _lib.load()
+    kv = _kv()
+    rows = (ctypes.c_int32 * 2)(0, 7)
+    f = lib.sv_verify_select
+
+    def call(B=1, P_max=1000, n_rows=2, k=FAKE, k_max=64, idx=FAKE, ws_bytes=1 << 30):
+        return f(FAKE, _lib.SV_BF16, B, 8, 32, 8, 128, ctypes.byref(kv), FAKE, P_max, None, rows, n_rows, 0.0, k,
+                 k_max, FAKE, FAKE, idx, None, FAKE, ws_bytes, None)
+    assert call(n_rows=0) == _lib.SV_E_INVALID           # selection needs scores
+    assert call(P_max=131073) == _lib.SV_E_UNSUPPORTED   # longer prefixes: the two separate calls
+    assert call(k=None) == _lib.SV_E_INVALID
+    assert call(idx=None) == _lib.SV_E_INVALID
+    assert call(k_max=-1) == _lib.SV_E_INVALID
+    assert call(ws_bytes=16) == _lib.SV_E_WORKSPACE
+    assert call(B=0) == _lib.SV_OK
 
 
 def test_topk_and_sparse_reject_bad_arguments():

@@ -28,7 +28,8 @@ __all__ = ["KVCache", "Workspace", "verify_attn", "topk_select", "sparse_draft_a
            "dense_draft_attn", "verify_workspace_size", "topk_workspace_size", "sparse_workspace_size",
            "dense_draft_workspace_size", "build_tree", "accept_commit", "verify_attn_per_head",
            "sparse_draft_attn_per_head", "select_sink_window", "timing_events", "SvError", "lib",
-           "validate_kv", "validate_tree", "validate_index", "ContractError", "verify_attn_noalloc"]
+           "validate_kv", "validate_tree", "validate_index", "ContractError", "verify_attn_noalloc",
+           "verify_select", "verify_select_workspace_size"]
 
 
 def lib() -> ctypes.CDLL:
@@ -229,6 +230,52 @@ def verify_attn_noalloc(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, 
                                         _ptr(prefix_len), P_max, _ptr(parent), rows_arr, len(rows), float(scale),
                                         _ptr(out), _ptr(scores) if rows else None, _stream(dev)))
     return out, (scores if rows else None)
+
+
+def verify_select_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, is_tree, n_score_rows, page_size=0) -> int:
+    return int(lib().sv_verify_select_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, int(bool(is_tree)),
+                                                     n_score_rows, int(page_size)))
+
+
+def verify_select(q: torch.Tensor, kv: KVCache, prefix_len: torch.Tensor, k: torch.Tensor, k_max: int, *,
+                  P_max: int, parent: Optional[torch.Tensor] = None, score_rows: Sequence[int] = (0,),
+                  scale: float = 0.0, out: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                  idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                  workspace: Optional[Workspace] = None):
+    """sv_verify_select: verify_attn then topk_select on its scores, fused.
+    -> (out [B][N][Hq][D], scores fp32 [B][P_max], idx int32 [B][k_max], count int32 [B])."""
+    _need(q.dim() == 4, "q must be [B][N][Hq][D]")
+    B, N, Hq, D = (int(x) for x in q.shape)
+    dev = q.device
+    _check_kv(kv, q.dtype, D, Hq, dev)
+    _check_i32(prefix_len, (B,), "prefix_len", dev)
+    _check_i32(parent, (B, N), "parent", dev)
+    _check_i32(k, (B,), "k", dev)
+    _check_like(out, tuple(q.shape), q.dtype, "out", dev)
+    _check_like(scores, (B, int(P_max)), torch.float32, "scores", dev)
+    _check_i32(idx, (B, int(k_max)), "idx", dev)
+    _check_i32(count, (B,), "count", dev)
+    rows = [int(r) for r in score_rows]
+    _need(len(rows) > 0, "verify_select needs at least one score row")
+    L = lib()
+    out = torch.empty_like(q) if out is None else out
+    scores = torch.empty((B, P_max), dtype=torch.float32, device=dev) if scores is None else scores
+    idx = torch.empty((B, k_max), dtype=torch.int32, device=dev) if idx is None else idx
+    count = torch.empty((B,), dtype=torch.int32, device=dev) if count is None else count
+    rows_arr = (ctypes.c_int32 * len(rows))(*rows)
+    dt = _dtype_code(q)
+    nbytes = verify_select_workspace_size(B, N, Hq, kv.Hkv, D, P_max, dt, parent is not None, len(rows),
+                                          kv.page_size if kv.page_table is not None else 0)
+    wptr, wlen = _ws(workspace, "verify_select").get(nbytes, dev)
+    kvs = kv.c_struct()
+    if _debug_checks():
+        _raise_on(validate_kv(kv, prefix_len, P_max=P_max, N=N))
+        if parent is not None:
+            _raise_on(validate_tree(parent))
+    _lib.check(L.sv_verify_select(_ptr(q), dt, B, N, Hq, kv.Hkv, D, ctypes.byref(kvs), _ptr(prefix_len), P_max,
+                                  _ptr(parent), rows_arr, len(rows), float(scale), _ptr(k), int(k_max), _ptr(out),
+                                  _ptr(scores), _ptr(idx), _ptr(count), wptr, wlen, _stream(dev)))
+    return out, scores, idx, count
 
 
 def topk_workspace_size(B, P_max) -> int:

@@ -21,6 +21,7 @@ EXPORTS = (
     "sv_accept_commit",
     "sv_validate_kv", "sv_validate_tree", "sv_validate_index",
     "sv_set_verify_timing_events", "sv_verify_attn_noalloc",
+    "sv_verify_select_workspace_size", "sv_verify_select",
 )
 
 
@@ -96,6 +97,11 @@ def load() -> ctypes.CDLL:
     lib.sv_build_tree.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.sv_accept_commit.restype = i32
     lib.sv_accept_commit.argtypes = [i32, i32, i32, i32, i32, kvp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sv_verify_select_workspace_size.restype = sz
+    lib.sv_verify_select_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.sv_verify_select.restype = i32
+    lib.sv_verify_select.argtypes = [vp, i32, i32, i32, i32, i32, i32, kvp, vp, i32, vp, vp, i32, f32,
+                                     vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.sv_verify_attn_noalloc.restype = i32
     lib.sv_verify_attn_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, i32, kvp, vp, i32, vp, vp, i32, f32,
                                            vp, vp, vp]

@@ -110,7 +110,8 @@ namespace {
 sv_status verify_common(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D, const sv_kv_cache* kv,
                         const int32_t* prefix_len, int P_max, const int32_t* parent, const int32_t* score_rows_host,
                         int n_score_rows, float softmax_scale, void* out, float* scores, void* workspace,
-                        size_t workspace_bytes, sv_stream stream, int head_scores) {
+                        size_t workspace_bytes, sv_stream stream, int head_scores,
+                        const sv::SelectArgs* sel = nullptr) {
   sv_status st;
   if ((st = check_dtype(dtype))) return st;
   if (B < 0) return fail(SV_E_INVALID, "B must be >= 0");
@@ -136,12 +137,18 @@ sv_status verify_common(const void* q, sv_dtype dtype, int B, int N, int Hq, int
   if ((st = check_kv(kv, B))) return st;
   const sv::VerifyPlan p = sv::plan_verify(B, N, Hq, Hkv, D, P_max, (int)dtype, parent != nullptr, n_score_rows,
                                            kv->page_table ? kv->page_size : 0);
-  if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
-    return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
+  const size_t need = sel ? sv::align_up(p.bytes) + sv::select_workspace_bytes(B) : p.bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+  sv::SelectArgs sa{};
+  if (sel) {
+    sa = *sel;
+    sa.ws = reinterpret_cast<char*>(workspace) + sv::align_up(p.bytes);
+  }
   const int e = sv::launch_verify(p, q, kv_args(kv), prefix_len, parent, score_rows_host, n_score_rows,
                                   resolve_scale(softmax_scale, D), out, scores, workspace, stream, g_ev_start,
-                                  g_ev_stop, 0, head_scores);
-  return hip_status(e, "sv_verify_attn launch");
+                                  g_ev_stop, 0, head_scores, sel ? &sa : nullptr);
+  return hip_status(e, sel ? "sv_verify_select launch" : "sv_verify_attn launch");
 }
 
 }  // namespace
@@ -164,6 +171,29 @@ sv_status sv_verify_attn_per_head(const void* q, sv_dtype dtype, int B, int N, i
                                   size_t workspace_bytes, sv_stream stream) {
   return verify_common(q, dtype, B, N, Hq, Hkv, D, kv, prefix_len, P_max, parent, score_rows_host, n_score_rows,
                        softmax_scale, out, head_scores, workspace, workspace_bytes, stream, 1);
+}
+
+size_t sv_verify_select_workspace_size(int B, int N, int Hq, int Hkv, int D, int P_max, sv_dtype dtype, int is_tree,
+                                       int n_score_rows, int page_size) {
+  const size_t v = sv_verify_workspace_size(B, N, Hq, Hkv, D, P_max, dtype, is_tree, n_score_rows, page_size);
+  if (v == 0 || n_score_rows <= 0 || P_max > sv::kSelectMaxP) return 0;
+  return sv::align_up(v) + sv::select_workspace_bytes(B);
+}
+
+sv_status sv_verify_select(const void* q, sv_dtype dtype, int B, int N, int Hq, int Hkv, int D,
+                           const sv_kv_cache* kv, const int32_t* prefix_len, int P_max, const int32_t* parent,
+                           const int32_t* score_rows_host, int n_score_rows, float softmax_scale, const int32_t* k,
+                           int k_max, void* out, float* scores, int32_t* idx, int32_t* count, void* workspace,
+                           size_t workspace_bytes, sv_stream stream) {
+  if (n_score_rows <= 0) return fail(SV_E_INVALID, "sv_verify_select needs score rows (n_score_rows >= 1)");
+  if (k_max < 0) return fail(SV_E_INVALID, "k_max must be >= 0");
+  if (P_max > sv::kSelectMaxP)
+    return fail(SV_E_UNSUPPORTED, "sv_verify_select takes prefixes up to %d (P_max = %d): use sv_verify_attn and "
+                "sv_topk_select", sv::kSelectMaxP, P_max);
+  if (B > 0 && (!k || (!idx && k_max > 0))) return fail(SV_E_INVALID, "k and idx must be non-NULL");
+  const sv::SelectArgs sel{k, k_max, idx, count, nullptr};
+  return verify_common(q, dtype, B, N, Hq, Hkv, D, kv, prefix_len, P_max, parent, score_rows_host, n_score_rows,
+                       softmax_scale, out, scores, workspace, workspace_bytes, stream, 0, &sel);
 }
 
 size_t sv_topk_workspace_size(int B, int P_max) {

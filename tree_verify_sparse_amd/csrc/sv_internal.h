@@ -54,13 +54,25 @@ struct KvArgs {
   long long seq_stride, num_slots;
 };
 
+// Selection fused into verification (sv_verify_select): the top-k of the
+// scores, with its own workspace of select_workspace_bytes(B).
+struct SelectArgs {
+  const int32_t* k;  // device [B]
+  int k_max;
+  int32_t* idx;      // device [B][k_max]
+  int32_t* count;    // device [B] or null
+  void* ws;
+};
+size_t select_workspace_bytes(int B);
+constexpr int kSelectMaxP = 32 * 4096;  // longest prefix the fused selection takes
+
 // Launchers (return a hipError_t as int; 0 = success).
 // len_bias: 0 for verification; -1 turns prefix_len into row counts of a dense
 // decode (N = 1: the query sees rows [0, prefix_len[b]), none when it is 0).
 int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const int32_t* prefix_len,
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
                   void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
-                  int len_bias = 0, int head_scores = 0);
+                  int len_bias = 0, int head_scores = 0, const SelectArgs* sel = nullptr);
 // Best-first draft trees from per-depth log-probabilities (one wave per sequence).
 int launch_build_tree(int B, int n, int max_depth, int n_cand, const double* lp, int32_t* parent, int32_t* depth,
                       int32_t* rank, void* stream);

@@ -23,6 +23,7 @@
 // only one fp32 per prefix key and KV head leaves the kernel.
 // Partial (m, l, o) per chunk are merged with log-sum-exp weights by a second
 // kernel, which also sums the per-KV-head score partials in a fixed order.
+#include "select_dev.h"
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -89,15 +90,24 @@ struct VerifyArgs {
   int B, N, Hq, Hkv, G, R, RB, Rpad, P_max, chunk, n_chunks, n_units;
   int tree, do_scores, prep_qbar;
   int qsplit;  // prep_qbar: partial sums per (sequence, KV head), each over kQbarPairs (row, head) pairs
-  int s_stride;  // row stride of the per-KV-head score partials: P_max + 32 (whole blocks are stored)
+  int s_stride;  // row stride of the per-KV-head score partials: P_max + 32 (whole blocks are stored), rounded up to 4
   int all_chunks;  // every chunk writes a partial (streaming kernel), else only chunks below P_b + N
   int ps_shift;  // log2(page_size) if it is a power of two, else -1
   float scale, scale_log2;
   int n_score_rows;
   int len_bias;  // 0 for verification; -1 for a decode over rows [0, prefix_len[b]) (see seq_prefix)
   int head_scores;  // 1: scores are per KV head, [B][Hkv][P_max] (no sum over the groups)
+  // fused selection (sv_verify_select): the merge's score workgroups run the
+  // two selection passes on the scores they sum (select_dev.h)
+  const int32_t* sel_k;  // device [B] requested k, or null: no selection
+  int sel_kmax;
+  int32_t* sel_idx;      // [B][sel_kmax]
+  int32_t* sel_count;    // [B] or null
+  SelWs selws;
   uint16_t score_rows[kMaxNodes];
 };
+
+
 
 // P_b of sequence b, clamped to [0, P_max], and in *L the length of its KV
 // range P_b + N.  A decode over the first n rows of a dense buffer passes n
@@ -1436,14 +1446,91 @@ __device__ __forceinline__ MergeAcc merge_acc(const MergeAcc& x, const MergeAcc&
   return MergeAcc{M, wx * x.l + wy * y.l, wx * x.o + wy * y.o};
 }
 
-template <typename T, int D, bool OB>
-__global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_row_wgs, int wpr) {
+// Fused selection, pass A on the merge's score workgroups (NT threads, one
+// per (sequence, block of sel_blk(P) prefix entries)): the block's scores are
+// summed from the per-KV-head partials (head order, as every score) and
+// written, then pass A runs on them (band from a sample of summed scores, the
+// block's entries at or above it to the selection workspace).  Pass B is the
+// next kernel.  Thread t sums the E entries base + E t + e and, for t < 256,
+// the SEG sample entries of segment t, each a 16-byte load per KV head: a
+// sample of 1024 entries (2048 for rows above 65536), half what a selection
+// over rows in memory takes, since every workgroup of the row sums it from
+// the partials of all KV heads.
+template <int NT, int E, int SEG>
+__device__ __forceinline__ void merge_select_block(SelShared& L, const VerifyArgs& a, int b, int blk, int P, int k) {
+  static_assert(E % 4 == 0 && SEG % 4 == 0, "16-byte pieces");
+  const int tid = threadIdx.x;
+  const int base = blk * E * NT;
+  const float* part = a.ws_s + (long long)b * a.Hkv * a.s_stride;  // rows of s_stride (a multiple of 4)
+  constexpr int NSEG = 256;  // sample segments
+  const bool samp = sel_multi(P, k);
+  const bool seg_t = samp && tid < NSEG;
+  const int p0 = seg_t ? sel_seg_start(tid, P, SEG, NSEG) : 0;
+  float x[E], smp[SEG];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = 0.f;
+#pragma unroll
+  for (int e = 0; e < SEG; ++e) smp[e] = 0.f;
+  // every load of a group of 8 KV heads before its sums (in head order, as
+  // every score is formed); a piece starting below P_b ends inside the row
+  // (rows hold P_max + 32 entries, rounded up to whole pieces)
+  constexpr int HG = 8;
+  for (int g0 = 0; g0 < a.Hkv; g0 += HG) {
+    f32x4 xv[HG][E / 4], sv[HG][SEG / 4];
+#pragma unroll
+    for (int j = 0; j < HG; ++j) {
+      const bool live = g0 + j < a.Hkv;
+      const float* pg = part + (long long)(live ? g0 + j : 0) * a.s_stride;
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        const int i = base + E * tid + 4 * q;
+        xv[j][q] = live && i < P ? *reinterpret_cast<const f32x4*>(pg + i) : f32x4{};
+      }
+#pragma unroll
+      for (int q = 0; q < SEG / 4; ++q)
+        sv[j][q] = live && seg_t ? *reinterpret_cast<const f32x4*>(pg + p0 + 4 * q) : f32x4{};
+    }
+#pragma unroll
+    for (int j = 0; j < HG; ++j) {
+      if (g0 + j < a.Hkv) {
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * q + e] += xv[j][q][e];
+#pragma unroll
+        for (int q = 0; q < SEG / 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) smp[4 * q + e] += sv[j][q][e];
+      }
+    }
+  }
+  float* srow = a.scores + (long long)b * a.P_max;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = base + E * tid + e;
+    if (i < P) srow[i] = x[e];
+    else x[e] = __builtin_nanf("");
+  }
+  if (!samp) return;
+  if (!seg_t)
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) smp[e] = __builtin_nanf("");
+  float t_lo, t_hi;
+  sel_band<NT>(L, smp, NSEG * SEG, P, k, &t_lo, &t_hi);
+  if (blk == 0 && tid == 0) a.selws.band[b] = SelBand{t_lo, t_hi, {0, 0}};
+  sel_compact<NT, E>(L, a.selws, b, blk, x, base, t_lo, t_hi, [](uint32_t* p, uint32_t v) { *p = v; });
+}
+
+template <typename T, int D, bool OB, bool SEL>
+__global__ void __launch_bounds__(SEL ? 512 : 256) verify_merge(const VerifyArgs a, int n_row_wgs, int wpr) {
+  constexpr int NT = SEL ? 512 : 256;
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < n_row_wgs) {
-    __shared__ MergeAcc red[4][32];
+    __shared__ MergeAcc red[NW][32];
     const int lane = tid & 63, wave = tid >> 6;
     const int sub = wave % wpr;
-    const int gr = (int)blockIdx.x * (4 / wpr) + wave / wpr;  // (b, g, row); uniform over a row's waves
+    const int gr = (int)blockIdx.x * (NW / wpr) + wave / wpr;  // (b, g, row); uniform over a row's waves
     if (gr >= a.B * a.Hkv * a.R) return;
     const int row = gr % a.R, bg = gr / a.R, g = bg % a.Hkv, b = bg / a.Hkv;
     // every chunk holds a partial (streaming kernel), else the chunks below P_b + N;
@@ -1515,6 +1602,16 @@ __global__ void __launch_bounds__(256) verify_merge(const VerifyArgs a, int n_ro
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[e] = (T)(acc.o[e] * inv);
     }
+  } else if constexpr (SEL) {
+    __shared__ SelShared L;
+    const int sw = (int)blockIdx.x - n_row_wgs;
+    const int b = sw / kSelMaxBlocks, blk = sw % kSelMaxBlocks;
+    if (b >= a.B) return;
+    int P, k;
+    sel_row_sizes(a.prefix_len, a.sel_k, b, a.P_max, a.sel_kmax, &P, &k);
+    if (blk * sel_blk(P) >= P) return;
+    if (sel_blk(P) == 4096) merge_select_block<NT, 4096 / NT, 8>(L, a, b, blk, P, k);
+    else merge_select_block<NT, 2048 / NT, 4>(L, a, b, blk, P, k);
   } else {
     const long long i0 = (long long)(blockIdx.x - n_row_wgs) * 256 + tid;
     if (i0 >= (long long)a.B * a.P_max) return;
@@ -1621,6 +1718,10 @@ __global__ void __launch_bounds__(256) verify_prep(const VerifyArgs a, int n_qba
 
 // ------------------------------------------------------------------------- host side
 
+size_t select_workspace_bytes(int B) { return sel_ws_bytes(B); }
+int launch_select_pass_b(const float* scores, int B, int P_max, const int32_t* prefix_len, const int32_t* k,
+                         int k_max, int32_t* idx, int32_t* count, const SelWs& w, hipStream_t st);
+
 VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtype, bool tree,
                        int n_score_rows, int page_size) {
   VerifyPlan p{};
@@ -1710,7 +1811,7 @@ VerifyPlan plan_verify(int B, int N, int Hq, int Hkv, int D, int P_max, int dtyp
   size_t off = 0;
   p.off_o = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * D * 4);
   p.off_ml = off; off = align_up(off + (size_t)B * Hkv * p.Rpad * p.n_chunks * 8);
-  p.off_s = off; off = align_up(off + (p.scores ? (size_t)B * Hkv * ((size_t)P_max + 32) * 4 : 0));
+  p.off_s = off; off = align_up(off + (p.scores ? (size_t)B * Hkv * (((size_t)P_max + 32 + 3) / 4 * 4) * 4 : 0));
   p.off_qbar = off; off = align_up(off + (p.prep_qbar ? (size_t)B * Hkv * p.qsplit * D * 4 : 0));
   p.off_anc = off; off = align_up(off + (tree ? (size_t)B * N * kAncWords * 4 : 0));
   p.bytes = off;
@@ -1780,20 +1881,42 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
   else if (p.RT == 2 && p.WR == 2) launch_main<T, D, 2, 2>(p, a, st, ev0, ev1);
   else launch_main<T, D, 2, 4>(p, a, st, ev0, ev1);
   const int wpr = p.n_chunks >= 16 ? 4 : 1;  // waves per merged row
+  const bool ob = p.treek || p.stream;        // the bf16 kernels write their o partials in bf16
+  if (a.sel_k) {
+    // fused selection: 512-thread workgroups, one per (sequence, selection block)
+    // after the row ones (pass A), then the selection's pass B kernel
+    const int n_row_wgs = (p.B * p.Hkv * p.R * wpr + 7) / 8;
+    const dim3 grid(n_row_wgs + p.B * kSelMaxBlocks);
+    if (ob) hipLaunchKernelGGL((verify_merge<T, D, true, true>), grid, dim3(512), 0, st, a, n_row_wgs, wpr);
+    else hipLaunchKernelGGL((verify_merge<T, D, false, true>), grid, dim3(512), 0, st, a, n_row_wgs, wpr);
+    const int e = (int)hipGetLastError();
+    if (e) return e;
+    return launch_select_pass_b(a.scores, p.B, p.P_max, a.prefix_len, a.sel_k, a.sel_kmax, a.sel_idx, a.sel_count,
+                                a.selws, st);
+  }
   const int n_row_wgs = (p.B * p.Hkv * p.R * wpr + 3) / 4;
   const long long n_s = p.scores ? ((long long)p.B * p.P_max + 255) / 256 : 0;
-  if (p.treek || p.stream)  // the bf16 kernels write their o partials in bf16
-    hipLaunchKernelGGL((verify_merge<T, D, true>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
+  if (ob)
+    hipLaunchKernelGGL((verify_merge<T, D, true, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs,
+                       wpr);
   else
-    hipLaunchKernelGGL((verify_merge<T, D, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs, wpr);
+    hipLaunchKernelGGL((verify_merge<T, D, false, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a,
+                       n_row_wgs, wpr);
   return (int)hipGetLastError();
 }
 
 int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const int32_t* prefix_len,
                   const int32_t* parent, const int32_t* score_rows, int n_score_rows, float scale,
                   void* out, float* scores, void* ws, void* stream, void* ev_start, void* ev_stop,
-                  int len_bias, int head_scores) {
+                  int len_bias, int head_scores, const SelectArgs* sel) {
   VerifyArgs a{};
+  if (sel) {
+    a.sel_k = sel->k;
+    a.sel_kmax = sel->k_max;
+    a.sel_idx = sel->idx;
+    a.sel_count = sel->count;
+    a.selws = sel_ws_at(sel->ws, p.B);
+  }
   a.q = q;
   a.out = out;
   a.kv = KvView{kv.k, kv.v, kv.page_table, kv.page_size, kv.max_pages, kv.seq_stride, kv.num_slots};
@@ -1808,7 +1931,7 @@ int launch_verify(const VerifyPlan& p, const void* q, const KvArgs& kv, const in
   a.scores = scores;
   a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.R = p.R; a.RB = p.RB; a.Rpad = p.Rpad;
   a.P_max = p.P_max; a.chunk = p.chunk; a.n_chunks = p.n_chunks;
-  a.s_stride = p.P_max + 32;
+  a.s_stride = (p.P_max + 32 + 3) / 4 * 4;  // whole 32-key blocks past P_max; rows 16-byte aligned
   a.n_units = p.B * p.Hkv * p.RB * p.n_chunks;
   a.all_chunks = p.treek ? 0 : 1;  // the tree kernel writes partials only for chunks below P_b + N
   a.ps_shift = -1;
