@@ -61,6 +61,7 @@ def parse():
                     help="fused: sv_verify_select (the selection inside the verification's last kernel); "
                          "separate: sv_verify_attn then sv_topk_select (same results)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweeps", action="store_true", help="skip the 4K..128K prefix sweep")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="before timing, run 3 plain device-to-device copies of this many MiB (a known-size "
@@ -403,6 +404,100 @@ def main():
                                       for a in (0.6, 0.7, 0.8, 0.9)},
                     "scope": "one attention layer (verify + selection, one draft decode); assumed alpha"}
 
+    # step-time distribution: the same K steps with an event between consecutive
+    # steps (each step's time is the gap between its two events)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    sev[0].record()
+    for i in range(K):
+        step(i)
+        sev[i + 1].record()
+    torch.cuda.synchronize()
+    st_us = np.array([sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(K)])
+    dist = {"p10_us": round(float(np.percentile(st_us, 10)), 2),
+            "median_us": round(float(np.median(st_us)), 2),
+            "p90_us": round(float(np.percentile(st_us, 90)), 2),
+            "how": "events between consecutive steps, a third pass of the K steps"}
+
+    # scoring overhead (Vegas §4): the verification alone (no selection) with no
+    # score rows, the workload's rows, and every verify row, each over the same K
+    # steps with the KV copies rotated
+    sweep_rows = None
+    if selection == "scores":
+        variants = {"0": [], str(len(rows)): rows, str(wl.N): list(range(wl.N))}
+        sweep_rows = {}
+        for name, rr in variants.items():
+            ra = (ctypes.c_int32 * max(1, len(rr)))(*rr)
+            wn = sv.verify_workspace_size(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, wl.P_max, dt, parent is not None,
+                                          len(rr), wl.page_size if pt is not None else 0)
+            wt = torch.empty(max(1, wn), dtype=torch.uint8, device=dev)
+            va = [a[:11] + (ra, len(rr), 0.0, out.data_ptr(), scores.data_ptr() if rr else None,
+                            wt.data_ptr(), wn, sp) for a in vargs]
+
+            def verify_only(i, va=va):
+                if L.sv_verify_attn(*va[i % copies]):
+                    raise RuntimeError(L.sv_last_error().decode())
+
+            sweep_rows[name] = round(timed(verify_only), 2)
+        base = sweep_rows["0"]
+        sweep_rows = {"verify_us_by_score_rows": sweep_rows,
+                      "overhead_pct": {k2: round((v2 / base - 1.0) * 100.0, 1) for k2, v2 in sweep_rows.items()},
+                      "what": "sv_verify_attn alone (fused scores, no selection), KV copies rotated"}
+
+    # one whole draft-verify iteration of a chain workload, measured: the target
+    # pass (verification + selection) and gamma = N - 1 draft decodes over the
+    # selected set, with seeded synthetic draft queries
+    iteration = None
+    if wl.parent is None and selection == "scores" and fused and wl.N > 1 and n_draft > 0:
+        gamma = wl.N - 1
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        gq = [(torch.randn((wl.B, wl.Hq, wl.D), generator=g, device=dev) / np.sqrt(wl.D)).to(q.dtype)
+              for _ in range(gamma)]
+        go = [torch.empty_like(x) for x in gq]
+        it_sparse = [[(gq[s].data_ptr(),) + dargs[c][0][1:12] + (go[s].data_ptr(),) + dargs[c][0][13:]
+                      for s in range(gamma)] for c in range(copies)]
+
+        def iter_sparse(i):
+            c = i % copies
+            st = f_fused(*fargs[c])
+            for a in it_sparse[c]:
+                st |= f_sparse(*a)
+            if st:
+                raise RuntimeError(L.sv_last_error().decode())
+
+        iteration = {"gamma": gamma, "sparse_us": round(timed(iter_sparse), 2)}
+        if draft_path != "compact":
+            cshape = (wl.B, max(1, kmax), wl.Hkv, wl.D)
+            ck = torch.empty(cshape, dtype=q.dtype, device=dev)
+            cv = torch.empty(cshape, dtype=q.dtype, device=dev)
+            dws_n = L.sv_dense_draft_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, max(1, kmax), dt)
+            dws = torch.empty(max(1, dws_n), dtype=torch.uint8, device=dev)
+            cargs = [(dt, wl.B, wl.Hkv, wl.D, ctypes.byref(kv), idx.data_ptr(), kmax, count.data_ptr(), kmax,
+                      ck.data_ptr(), cv.data_ptr(), max(1, kmax), sp) for kv in kvs]
+        it_dense = [(gq[s].data_ptr(), dt, wl.B, wl.Hq, wl.Hkv, wl.D, ck.data_ptr(), cv.data_ptr(),
+                     max(1, kmax), count.data_ptr(), 0.0, go[s].data_ptr(), dws.data_ptr(), dws_n, sp)
+                    for s in range(gamma)]
+
+        def iter_compact(i):
+            c = i % copies
+            st = f_fused(*fargs[c]) | f_compact(*cargs[c])
+            for a in it_dense:
+                st |= f_dense(*a)
+            if st:
+                raise RuntimeError(L.sv_last_error().decode())
+
+        iteration["compact_us"] = round(timed(iter_compact), 2)
+        best = min(v2 for k2, v2 in iteration.items() if k2.endswith("_us"))
+        iteration["tokens_per_ms"] = {f"alpha={a}": round(tokens_per_round(a, gamma) / best * 1e3, 2)
+                                      for a in (0.6, 0.7, 0.8, 0.9)}
+        iteration["scope"] = "one attention layer: verification + selection + gamma draft decodes; assumed alpha"
+
+    sweeps = {"step_time_distribution": dist, "scoring_overhead": sweep_rows, "measured_iteration": iteration}
+    if args.workload == 2 and not args.no_sweeps:
+        sweeps["prefix_sweep"] = prefix_sweep(sv, L, _lib, dev, sp, max(20, K // 4))
+    sweeps["hbm_reference"] = hbm_reference(dev)
+
     value = step_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": "verify+select+sparse-draft us/step and HBM GB/s (% peak) at 32k ctx, 1 GPU",
@@ -426,9 +521,13 @@ def main():
                       "build_tree_us": round(build_us, 2) if build_us is not None else None,
                       "tpt_projection": tpt_rows,
                       "select_and_draft_rooflines": other_roofs},
+        "measurements": sweeps,
     }
-    if not args.no_cpu_baseline and args.workload in (1, 2, 3):
-        res["cpu_baseline"] = cpu_baseline(wl, step_bytes, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        if args.workload in (1, 2, 3):
+            res["cpu_baseline"] = cpu_baseline(wl, step_bytes, args.cpu_seconds)
+        else:
+            res["cpu_baseline"] = cpu_baseline_sampled(wl, step_bytes, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -449,12 +548,160 @@ def _traffic(workload: int):
     return None
 
 
+def tokens_per_round(alpha: float, gamma: int) -> float:
+    """Expected tokens of one draft-verify round (KnapSpec §2): the accepted
+    drafts plus the target's own token, (1 - alpha^(gamma+1)) / (1 - alpha)."""
+    return gamma + 1.0 if alpha == 1.0 else (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
+
+
+def prefix_sweep(sv, L, _lib, dev, sp, steps):
+    """The 32k layer's step (verification + fused selection + one sparse draft
+    decode; B=1, 32 query / 8 KV heads, D=128, bf16, chain of 8 verify queries,
+    score rows {0, 7}, k=2048) at prefixes 4K..128K (KnapSpec §1: attention
+    time linear in the context).  Keys and values are seeded N(0, 1/D) draws
+    made on the device; each point rotates enough cache copies that about 1 GB
+    streams between reuses (the 256 MB last-level cache holds no prefix)."""
+    import numpy as np
+    import torch
+    Hq, Hkv, D, N, k = 32, 8, 128, 8, 2048
+    rows = [0, N - 1]
+    dt = _lib.SV_BF16
+    row_b = Hkv * D * 2
+    pool_rows = 2 * (131072 + N)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    kpool = (torch.randn((pool_rows, Hkv, D), generator=g, device=dev) / np.sqrt(D)).to(torch.bfloat16)
+    vpool = (torch.randn((pool_rows, Hkv, D), generator=g, device=dev) / np.sqrt(D)).to(torch.bfloat16)
+    q = (torch.randn((1, N, Hq, D), generator=g, device=dev) / np.sqrt(D)).to(torch.bfloat16)
+    dq = (torch.randn((1, Hq, D), generator=g, device=dev) / np.sqrt(D)).to(torch.bfloat16)
+    out, dout = torch.empty_like(q), torch.empty_like(dq)
+    ra = (ctypes.c_int32 * 2)(*rows)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pts = []
+    for P in (4096, 8192, 16384, 32768, 65536, 131072):
+        ncp = max(1, min(64, pool_rows // (P + N)))
+        kvs = [_lib.SvKvCache(kpool.data_ptr() + c * (P + N) * row_b, vpool.data_ptr() + c * (P + N) * row_b,
+                              None, 1, 0, P + N, P + N) for c in range(ncp)]
+        Pt = torch.tensor([P], dtype=torch.int32, device=dev)
+        kt = torch.tensor([k], dtype=torch.int32, device=dev)
+        scores = torch.empty((1, P), dtype=torch.float32, device=dev)
+        idx = torch.empty((1, k), dtype=torch.int32, device=dev)
+        cnt = torch.empty((1,), dtype=torch.int32, device=dev)
+        fn = sv.verify_select_workspace_size(1, N, Hq, Hkv, D, P, dt, False, 2, 0)
+        fw = torch.empty(max(1, fn), dtype=torch.uint8, device=dev)
+        sn = sv.sparse_workspace_size(1, Hq, Hkv, D, k)
+        sw = torch.empty(max(1, sn), dtype=torch.uint8, device=dev)
+        fa = [(q.data_ptr(), dt, 1, N, Hq, Hkv, D, ctypes.byref(kv), Pt.data_ptr(), P, None, ra, 2, 0.0,
+               kt.data_ptr(), k, out.data_ptr(), scores.data_ptr(), idx.data_ptr(), cnt.data_ptr(), fw.data_ptr(),
+               fn, sp) for kv in kvs]
+        da = [(dq.data_ptr(), dt, 1, Hq, Hkv, D, ctypes.byref(kv), idx.data_ptr(), k, cnt.data_ptr(), k, 0.0,
+               dout.data_ptr(), sw.data_ptr(), sn, sp) for kv in kvs]
+
+        def one(i):
+            c = i % ncp
+            if L.sv_verify_select(*fa[c]) | L.sv_sparse_draft_attn(*da[c]):
+                raise RuntimeError(L.sv_last_error().decode())
+
+        for i in range(5):
+            one(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            one(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        byts = (P + N) * row_b * 2 + q.nbytes * 2 + P * 4 + (P * 4 + k * 4) + (k * row_b * 2 + 2 * dq.nbytes + k * 4)
+        pts.append({"prefix": P, "us_per_step": round(us, 2), "GBs": round(byts / us / 1e3, 1),
+                    "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4), "kv_copies_rotated": ncp})
+        del scores, idx, cnt, fw, sw
+    del kpool, vpool
+    torch.cuda.empty_cache()
+    return {"points": pts, "steps_per_point": steps,
+            "step": "sv_verify_select + one sv_sparse_draft_attn (the 32k layer's shape)"}
+
+
+def hbm_reference(dev):
+    """Bandwidths of plain library kernels on this GPU, for scale: a 2 GiB
+    device-to-device copy (bytes read + written) and a float32 sum over 2 GiB
+    of bfloat16 (bytes read)."""
+    import torch
+    n = 1 << 30
+    x = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, byts, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(byts * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+    r = {"copy_GBs": rate(lambda: y.copy_(x), 2 * x.nbytes),
+         "sum_read_GBs": rate(lambda: x.sum(dtype=torch.float32), x.nbytes),
+         "what": "torch copy_ of 2 GiB (read + write bytes) and torch sum over 2 GiB bf16 (read bytes)"}
+    del x, y
+    torch.cuda.empty_cache()
+    return r
+
+
 def tpt(alpha: float, gamma: int, t_draft: float, t_target: float) -> float:
     """Tokens per unit of time of a draft-verify round (KnapSpec §2, the TPT
     metric): (1 - alpha^(gamma+1)) / (1 - alpha) expected tokens (gamma + 1 at
     alpha = 1) over gamma draft steps and one target pass."""
     tokens = gamma + 1.0 if alpha == 1.0 else (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
     return tokens / (gamma * t_draft + t_target)
+
+
+def cpu_baseline_sampled(wl, step_bytes, target_s):
+    """The CPU oracle on a per-(sequence, KV head) sample of a workload too
+    large for full steps: each sample is one sequence's slice for one KV head
+    (its group of query heads, its prefix rows, its draft query) run as a whole
+    step; the full step's time is estimated as the mean sample time times the
+    number of (sequence, KV head) pairs.  The selection runs once per sample
+    (on that head's scores) instead of once per sequence, so the estimate is a
+    little above a full step's CPU time."""
+    import numpy as np
+    import oracle
+    from types import SimpleNamespace
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    G = wl.Hq // wl.Hkv
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.Hkv)]
+    order = np.random.default_rng(11).permutation(len(pairs))
+    t0 = time.perf_counter()
+    taken = []
+    for j in order:
+        b, h = pairs[j]
+        Pb = int(wl.P[b])
+        sl = wl.slot(b, np.arange(Pb + wl.N))
+        sub = SimpleNamespace(
+            dtype=wl.dtype, B=1, Hq=G, Hkv=1, D=wl.D, N=wl.N, P=np.array([Pb], np.int32), P_max=Pb,
+            scale=wl.scale, layout="contiguous", seq_stride=Pb + wl.N, page_size=1, page_table=None,
+            num_slots=Pb + wl.N, q=wl.q[b:b + 1, :, h * G:(h + 1) * G], k=wl.k[sl, h:h + 1],
+            v=wl.v[sl, h:h + 1], parent=None if wl.parent is None else wl.parent[b:b + 1],
+            score_rows=wl.score_rows, k_sel=wl.k_sel[b:b + 1], dq=wl.dq[:1, b:b + 1, h * G:(h + 1) * G],
+            max_pages=0)
+        ts = time.perf_counter()
+        oracle.run_step(sub)
+        taken.append((b, h, Pb, time.perf_counter() - ts))
+        if time.perf_counter() - t0 >= target_s:
+            break
+    # scale by prefix length: a sample's time is close to linear in its prefix
+    per_pos = sum(t for *_, t in taken) / sum(p + wl.N for _, _, p, _ in taken)
+    est = per_pos * float((wl.P.astype(np.int64) + wl.N).sum()) * wl.Hkv
+    return {"value": round(step_bytes / est / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seconds_per_step_estimated": round(est, 3), "numpy": np.__version__, "host_cpus": os.cpu_count(),
+            "sample": f"{len(taken)} of {len(pairs)} (sequence, KV head) slices run as whole steps (verify rows, "
+                      f"scores, top-k, first draft step), {sum(t for *_, t in taken):.1f} s; full step estimated "
+                      f"as seconds per (prefix + verify) position x all positions x KV heads"}
 
 
 def cpu_baseline(wl, step_bytes, target_s):
