@@ -50,3 +50,43 @@ def test_build_tree_edges_and_ties():
     # equal log-probabilities everywhere: order decided by parent id, then rank
     _check(np.full((2, 5, 4), -1.0), 60, 4)
     _check(np.array([[[0.0, 0.0], [-1.0, -1.0], [-1.0, -2.0]]]), 5, 2)
+
+
+def _reachable(nc, depth):
+    reach, lev = 1, 1
+    for _ in range(depth):
+        lev = min(lev * nc, 1 << 20)
+        reach += lev
+    return reach
+
+
+@pytest.mark.parametrize("kind", ["plain", "quarter_ties", "fine_ties", "all_equal", "wide", "zero_logprobs"])
+def test_build_tree_random_shapes(kind):
+    """Random budgets, depths and candidate counts, with log-probabilities
+    rounded to coarse and fine grids (many exactly equal scores, also at the
+    budget's threshold), constant rows, scores spread over hundreds of units,
+    and zero log-probabilities (a child or sibling scoring exactly what its
+    parent or elder sibling scores)."""
+    r = np.random.default_rng(["plain", "quarter_ties", "fine_ties", "all_equal", "wide",
+                               "zero_logprobs"].index(kind) + 500)
+    for t in range(12):
+        depth = int(r.integers(1, 10))
+        nc = int(r.integers(1, 40))
+        n = int(r.integers(1, min(256, _reachable(nc, depth)) + 1))
+        B = int(r.integers(1, 4))
+        lps = []
+        for _ in range(B):
+            lp = depth_logprobs(r, depth, n_cand=nc)
+            if kind == "quarter_ties":
+                lp = np.round(lp * 4) / 4
+            elif kind == "fine_ties":
+                lp = np.round(lp * 64) / 64
+            elif kind == "all_equal":
+                lp = np.full_like(lp, -0.75)
+            elif kind == "wide":
+                lp = lp * 30.0
+            elif kind == "zero_logprobs":
+                lp[1:, 0] = 0.0
+            lps.append(lp)
+        print(f"[case] {kind} #{t}: B={B} n={n} depth={depth} n_cand={nc}", flush=True)
+        _check(np.stack(lps), n, depth)

@@ -4,17 +4,34 @@
 // node budget is reached), so the parent array the verify pass needs never
 // makes a host round trip.
 //
-// One wave per sequence.  The live candidates sit in registers, slot j in
-// lane j % 64: each expansion takes one (its slot is reused by the new node's
-// rank-0 child) and adds at most one (the parent's next rank), so at most
-// n_nodes slots are ever used.  The best candidate -- highest fp64 score,
-// then lower parent id, then lower rank -- is found with each lane comparing
-// its slots and a DPP wave reduction over (score, key), the key packing
-// parent, rank, slot and depth (lower wins; slots are unique).
-// Scores are the same fp64 sums, in the same order, as a sequential
-// implementation, so the tree is identical bit for bit.  The log-probabilities
-// and the growing tree stay in LDS; global memory is touched once before and
-// once after the expansions.
+// A node is a rank sequence (r_1 .. r_d) with score S = sum_j lp[j][r_j]
+// (fp64, accumulated from the root in depth order, as the sequential
+// expansion adds a candidate's log-probability to its parent's score).  Log-
+// probabilities are at most 0 and each depth's list is sorted, so a node's
+// parent and its lower-rank siblings score at least as high as the node, and
+// the sequential expansion takes nodes in the order
+//     higher score first; equal scores: the parent taken earlier first, then
+//     the lower rank
+// (an order in which every candidate comes after the node that offered it, so
+// always taking the best offered candidate follows it exactly).  The tree is
+// therefore the first n - 1 sequences of that order, and it is built without
+// the sequential loop:
+//   1. a threshold tau with n - 1 <= |{S >= tau}| <= kBtCap is found by
+//      counting, in each of the 16 waves, the sequences at or above one trial
+//      value (level by level: a node at depth d - 1 with score s has exactly
+//      the children r with s + lp[d][r] >= tau, a prefix of the sorted list);
+//      the first round tries the best depth-1 score and 15 geometrically
+//      spaced values below it, later rounds 16 evenly spaced values inside the
+//      bracket found so far;
+//   2. the wave that counted the chosen value holds C = {S >= tau}, which
+//      contains the tree; every node of C gets its place in the order by
+//      counting the nodes before it (equal scores compare parents, walking
+//      up), and the first n - 1 places are numbered 1 .. n - 1.
+// If no trial value isolates at most kBtCap sequences (many exactly equal
+// scores at the threshold), wave 0 runs the sequential expansion instead.
+// No atomics: the result is the same bits on every run, and the same tree as
+// the sequential expansion.
+#include "select_dev.h"
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -27,6 +44,156 @@ struct BuildArgs {
   int32_t* rank;     // [B][n] or null
   int n, max_depth, n_cand;
 };
+
+constexpr int kLpLds = 4096;   // log-probabilities kept in LDS when they fit (32 KB)
+constexpr int kBtWaves = 16;   // trial thresholds counted at once (one per wave)
+constexpr int kBtCap = 384;    // sequences a wave holds for one trial value
+constexpr int kBtRounds = 8;   // bracketing rounds before the sequential expansion
+constexpr int kBtParts = 4;    // threads counting the places of one node
+constexpr uint32_t kBtRoot = 0xffffu;
+
+struct BtShared {
+  double lp[kLpLds];
+  double S[kBtWaves][kBtCap];            // scores
+  uint32_t meta[kBtWaves][kBtCap];       // parent's index in the same list << 16 | rank
+  uint16_t dep[kBtWaves][kBtCap];        // depth
+  int pos[kBtCap];                       // place in the expansion order
+  int part[kBtParts][kBtCap];            // per-slice counts: before | equal << 16
+  int mark[kBtWaves][kBtCap + 64];       // child placement marks
+  int cnt[kBtWaves];
+  double tau[kBtWaves];
+  // sequential expansion
+  double cum[kMaxNodes];
+  int np_[kMaxNodes], nd_[kMaxNodes], nr_[kMaxNodes];
+};
+
+// The next double above a finite x.
+__device__ __forceinline__ double next_up(double x) {
+  if (x == 0.0) return __longlong_as_double(1LL);
+  const long long u = __double_as_longlong(x);
+  return __longlong_as_double(x > 0.0 ? u + 1 : u - 1);
+}
+
+// Number of ranks r < nc with sv + row[r] >= tau (a prefix of the sorted
+// list): an 8-way search, each step's probes issued together.
+__device__ __forceinline__ int bt_count(const double* row, int nc, double sv, double tau) {
+  int c = 0;
+  for (int span = nc > 64 ? 64 : (nc > 8 ? 8 : 1); span >= 1; span >>= 3) {
+    bool t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = c + span * (k + 1) - 1;
+      t[k] = i < nc && sv + row[i < nc ? i : 0] >= tau;
+    }
+    int m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m += t[k] ? 1 : 0;
+    c += span * m;
+  }
+  return c;
+}
+
+// Inclusive max over lanes 0 .. lane (DPP, no LDS).
+__device__ __forceinline__ int wave_incl_max(int x) {
+  x = max(x, (int)__builtin_amdgcn_update_dpp(-1, x, 0x111, 0xf, 0xf, false));
+  x = max(x, (int)__builtin_amdgcn_update_dpp(-1, x, 0x112, 0xf, 0xf, false));
+  x = max(x, (int)__builtin_amdgcn_update_dpp(-1, x, 0x114, 0xf, 0xf, false));
+  x = max(x, (int)__builtin_amdgcn_update_dpp(-1, x, 0x118, 0xf, 0xf, false));
+  x = max(x, (int)__builtin_amdgcn_update_dpp(-1, x, 0x142, 0xa, 0xf, false));
+  x = max(x, (int)__builtin_amdgcn_update_dpp(-1, x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+// The sequences with score >= tau, level by level, into one wave's lists;
+// their number, or kBtCap + 1 as soon as there would be more than kBtCap.
+// mark: the wave's kBtCap + 64 LDS words for placing children.
+__device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, double* S, uint32_t* meta,
+                         uint16_t* dep, int* mark, int lane) {
+  int cnt = 0;
+  int p0 = -1, np = 1;  // the previous level: first index and size (the root alone at first)
+  for (int d = 1; d <= max_depth; ++d) {
+    const double* row = lp + (long long)d * nc;
+    int level = 0;
+    for (int base = 0; base < np; base += 64) {
+      const int i = base + lane;
+      const bool act = i < np;
+      const int v = p0 < 0 ? -1 : p0 + i;
+      const double sv = (act && v >= 0) ? S[v] : 0.0;
+      const int c = act ? bt_count(row, nc, sv, tau) : 0;
+      const int incl = (int)sel_wave_scan((uint32_t)c);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (cnt + level + tot > kBtCap) return kBtCap + 1;
+      const int o = cnt + level + incl - c;  // this lane's first child's place
+      const uint32_t pm = (uint32_t)(v < 0 ? kBtRoot : (uint32_t)v) << 16;
+      if (wave_max_u32((uint32_t)c) <= 4) {
+        // few children per parent: each lane writes its own (reads issued together)
+        double ch[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ch[j] = sv + row[j < c ? j : 0];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < c) {
+            S[o + j] = ch[j];
+            meta[o + j] = pm | (uint32_t)j;
+            dep[o + j] = (uint16_t)d;
+          }
+      } else {
+        // children in lane order: lane l's occupy [incl_l - c_l, incl_l) of
+        // this batch.  Each parent marks its first child's place; an
+        // inclusive max over the marks gives every place its parent lane.
+        for (int t = lane; t < tot; t += 64) mark[t] = -1;
+        __builtin_amdgcn_wave_barrier();
+        if (c > 0) mark[incl - c] = lane;
+        __builtin_amdgcn_wave_barrier();
+        int carry = -1;
+        for (int t0 = 0; t0 < tot; t0 += 64) {
+          const int t = t0 + lane;
+          int pl = wave_incl_max(t < tot ? mark[t] : -1);
+          pl = max(pl, carry);  // every place below tot has a parent; lanes past it read lane 0
+          carry = __builtin_amdgcn_readlane(pl, 63);
+          pl = max(pl, 0);
+          // the parent lane's score, index and first place
+          const double psv = __shfl(sv, pl);
+          const int pv = __shfl(v, pl);
+          const int pfirst = __shfl(incl - c, pl);
+          if (t < tot) {
+            const int r = t - pfirst;
+            const int w = cnt + level + t;
+            S[w] = psv + row[r];
+            meta[w] = (uint32_t)(pv < 0 ? kBtRoot : (uint32_t)pv) << 16 | (uint32_t)r;
+            dep[w] = (uint16_t)d;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      level += tot;
+    }
+    // one wave: its LDS accesses complete in order, so the next level reads
+    // these writes without a barrier
+    __builtin_amdgcn_wave_barrier();
+    if (level == 0) break;
+    p0 = cnt;
+    np = level;
+    cnt += level;
+  }
+  return cnt;
+}
+
+// u before v (u != v) in the expansion order: higher score; equal scores, the
+// parent taken earlier (the same comparison one level up), then the lower rank.
+__device__ __forceinline__ bool bt_before(const double* S, const uint32_t* meta, int u, int v) {
+  for (;;) {
+    const double su = S[u], sv = S[v];
+    if (su != sv) return su > sv;
+    const uint32_t mu = meta[u], mv = meta[v];
+    const uint32_t pu = mu >> 16, pv = mv >> 16;
+    if (pu == pv) return (mu & 0xffffu) < (mv & 0xffffu);
+    if (pu == kBtRoot) return true;
+    if (pv == kBtRoot) return false;
+    u = (int)pu;
+    v = (int)pv;
+  }
+}
 
 __device__ __forceinline__ bool cand_better(double s1, uint32_t k1, double s2, uint32_t k2) {
   return s1 > s2 || (s1 == s2 && k1 < k2);
@@ -47,26 +214,17 @@ __device__ __forceinline__ void cand_dpp(double& s, uint32_t& k) {
   }
 }
 
-constexpr int kLpLds = 4096;  // log-probabilities kept in LDS when they fit (32 KB)
-
-template <bool IN_LDS>
-__global__ void __launch_bounds__(64) build_tree(const BuildArgs a) {
-  __shared__ double lps[kLpLds];     // the sequence's log-probabilities (when they fit)
-  __shared__ double cum[kMaxNodes];  // node scores
-  __shared__ int np_[kMaxNodes], nd_[kMaxNodes], nr_[kMaxNodes];  // node parent, depth, rank
-  constexpr int SPL = kMaxNodes / 64;  // candidate slots per lane: slot j lives in lane j % 64, entry j / 64
-  const int b = blockIdx.x, lane = threadIdx.x, n = a.n, nc = a.n_cand;
-  const int nlp = (a.max_depth + 1) * nc;
-  const double* lpg = a.lp + (long long)b * nlp;
-  // every expansion reads two log-probabilities: from LDS when they fit (a
-  // separate instantiation, so the reads are plain LDS reads, not flat ones)
-  if constexpr (IN_LDS)
-    for (int j = lane; j < nlp; j += 64) lps[j] = lpg[j];
-  const double* lp = IN_LDS ? lps : lpg;
-  const long long o = (long long)b * n;
+// The sequential expansion by one wave, for thresholds no trial value
+// isolates.  The live candidates sit in registers, slot j in lane j % 64: each
+// expansion takes one (its slot is reused by the new node's rank-0 child) and
+// adds at most one (the parent's next rank), so at most n slots are ever used.
+// The best candidate is found with each lane comparing its slots and a DPP
+// wave reduction over (score, key), the key packing parent, rank, slot and
+// depth (lower wins; slots are unique).
+__device__ void bt_sequential(const double* lp, const double* lpg, int n, int max_depth, int nc, BtShared& L,
+                              int lane) {
+  constexpr int SPL = kMaxNodes / 64;
   const double ninf = -__builtin_inf();
-  // candidate (score, key) in registers; key = parent << 24 | rank << 16 | slot << 8 | depth
-  // (lower wins among equal scores: parent, then rank; slots are unique)
   double cs[SPL];
   uint32_t ck[SPL];
 #pragma unroll
@@ -75,7 +233,7 @@ __global__ void __launch_bounds__(64) build_tree(const BuildArgs a) {
     ck[u] = 0xffffffffu;
   }
   int nslots = 0;
-  if (n > 1 && a.max_depth >= 1) {
+  if (n > 1 && max_depth >= 1) {
     if (lane == 0) {
       cs[0] = 0.0 + lpg[1 * nc + 0];
       ck[0] = 1u;  // parent 0, rank 0, slot 0, depth 1
@@ -83,12 +241,12 @@ __global__ void __launch_bounds__(64) build_tree(const BuildArgs a) {
     nslots = 1;
   }
   if (lane == 0) {
-    np_[0] = -1;
-    nd_[0] = 0;
-    nr_[0] = 0;
-    cum[0] = 0.0;
+    L.np_[0] = -1;
+    L.nd_[0] = 0;
+    L.nr_[0] = 0;
+    L.cum[0] = 0.0;
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
   for (int i = 1; i < n; ++i) {
     double bs = cs[0];
     uint32_t bk = ck[0];
@@ -112,16 +270,14 @@ __global__ void __launch_bounds__(64) build_tree(const BuildArgs a) {
     // the host checked that n nodes are reachable, so a live candidate exists
     const int p = (int)(key >> 24), r = (int)((key >> 16) & 0xffu), slot = (int)((key >> 8) & 0xffu),
               d = (int)(key & 0xffu);
-    const bool child = d < a.max_depth, sib = r + 1 < nc;
-    // the three reads the new candidates need, issued together (indices kept in range)
+    const bool child = d < max_depth, sib = r + 1 < nc;
     const double lp_child = lp[(child ? d + 1 : d) * nc + 0];
     const double lp_sib = lp[d * nc + (sib ? r + 1 : r)];
-    const double cum_p = cum[p];
+    const double cum_p = L.cum[p];
     const double s_child = child ? sc + lp_child : ninf;
     const uint32_t k_child = child ? (((uint32_t)i << 24) | ((uint32_t)slot << 8) | (uint32_t)(d + 1)) : 0xffffffffu;
     const double s_sib = cum_p + lp_sib;
     const uint32_t k_sib = ((uint32_t)p << 24) | ((uint32_t)(r + 1) << 16) | ((uint32_t)nslots << 8) | (uint32_t)d;
-    // the new node's rank-0 child takes the slot; the parent's next rank a new one
 #pragma unroll
     for (int u = 0; u < SPL; ++u) {
       if (slot == u * 64 + lane) {
@@ -134,21 +290,141 @@ __global__ void __launch_bounds__(64) build_tree(const BuildArgs a) {
       }
     }
     if (lane == 0) {
-      np_[i] = p;
-      nd_[i] = d;
-      nr_[i] = r;
-      cum[i] = sc;
+      L.np_[i] = p;
+      L.nd_[i] = d;
+      L.nr_[i] = r;
+      L.cum[i] = sc;
     }
     nslots += sib ? 1 : 0;
-    // one wave: its LDS accesses complete in order, so the next expansion sees
-    // these writes without a barrier (a barrier would also wait on memory)
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+template <bool IN_LDS>
+__global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
+  __shared__ BtShared L;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = a.n, nc = a.n_cand;
+  const int nlp = (a.max_depth + 1) * nc;
+  const double* lpg = a.lp + (long long)b * nlp;
+  if constexpr (IN_LDS)
+    for (int j = tid; j < nlp; j += kBtWaves * 64) L.lp[j] = lpg[j];
+  const double* lp = IN_LDS ? L.lp : lpg;
+  const long long o = (long long)b * n;
+  if (tid == 0) {
+    a.parent[o] = -1;
+    if (a.depth) a.depth[o] = 0;
+    if (a.rank) a.rank[o] = 0;
+  }
+  if (n <= 1) return;  // the root alone (a uniform exit: no barrier follows)
   __syncthreads();
-  for (int t = lane; t < n; t += 64) {
-    a.parent[o + t] = np_[t];
-    if (a.depth) a.depth[o + t] = nd_[t];
-    if (a.rank) a.rank[o + t] = nr_[t];
+
+  // 1. bracket the threshold
+  const double hi = lp[1 * nc + 0];  // the best depth-1 score: no sequence scores higher
+  double lo_ok = -__builtin_inf();   // a value at which more than kBtCap sequences score at least as high
+  double hi_bad = next_up(hi);       // fewer than n - 1 at or above it (none above hi)
+  double geo = 0.125;
+  int win = -1;
+  for (int rnd = 0; rnd < kBtRounds && win < 0; ++rnd) {
+    double tau;
+    if (lo_ok == -__builtin_inf()) {
+      double g = geo;
+      for (int w = 1; w < wave; ++w) g *= 1.6;
+      tau = wave == 0 ? hi : hi - g;
+    } else {
+      tau = hi_bad - (hi_bad - lo_ok) * (double)(wave + 1) / (double)(kBtWaves + 1);
+    }
+    const int c = bt_expand(lp, nc, a.max_depth, tau, L.S[wave], L.meta[wave], L.dep[wave], L.mark[wave], lane);
+    if (lane == 0) {
+      L.cnt[wave] = c;
+      L.tau[wave] = tau;
+    }
+    __syncthreads();
+    int w = -1;
+    for (int j = 0; j < kBtWaves; ++j)
+      if (L.cnt[j] >= n - 1) {
+        w = j;
+        break;
+      }
+    if (w >= 0) {
+      if (L.cnt[w] <= kBtCap) {
+        win = w;
+      } else {
+        lo_ok = L.tau[w];
+        if (w > 0) hi_bad = L.tau[w - 1];
+      }
+    } else if (lo_ok == -__builtin_inf()) {
+      for (int j = 0; j < kBtWaves; ++j) geo *= 1.6;
+    } else {
+      hi_bad = L.tau[kBtWaves - 1];
+    }
+    if (win < 0) __syncthreads();  // the lists are rewritten by the next round
+  }
+
+  if (win >= 0) {
+    // 2. places in the expansion order; the first n - 1 become nodes 1 .. n - 1
+    const int M = L.cnt[win];
+    const double* S = L.S[win];
+    const uint32_t* meta = L.meta[win];
+    // K threads per node, each counting over one slice of the list
+    const int K = min(kBtParts, (kBtWaves * 64) / M);
+    const int span = (M + K - 1) / K;
+    if (tid < K * M) {
+      const int v = tid % M, k = tid / M;
+      const int u0 = k * span, u1 = min(M, u0 + span);
+      const double sv = S[v];
+      int pos = 0, ties = 0;
+      int u = u0;
+      for (; u + 8 <= u1; u += 8) {
+        double x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = S[u + j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pos += x[j] > sv ? 1 : 0;
+          ties += x[j] == sv ? 1 : 0;
+        }
+      }
+      for (; u < u1; ++u) {
+        const double su = S[u];
+        pos += su > sv ? 1 : 0;
+        ties += su == sv ? 1 : 0;
+      }
+      L.part[k][v] = pos | (ties << 16);
+    }
+    __syncthreads();
+    for (int v = tid; v < M; v += kBtWaves * 64) {
+      int pos = 0, ties = 0;
+      for (int k = 0; k < K; ++k) {
+        pos += L.part[k][v] & 0xffff;
+        ties += L.part[k][v] >> 16;
+      }
+      if (ties > 1) {  // equal scores (itself included once): the order one level up decides
+        const double sv = S[v];
+        for (int u = 0; u < M; ++u)
+          pos += (u != v && S[u] == sv && bt_before(S, meta, u, v)) ? 1 : 0;
+      }
+      L.pos[v] = pos;
+    }
+    __syncthreads();
+    for (int v = tid; v < M; v += kBtWaves * 64) {
+      const int p = L.pos[v];
+      if (p < n - 1) {
+        const uint32_t m = meta[v];
+        const uint32_t pv = m >> 16;
+        a.parent[o + p + 1] = pv == kBtRoot ? 0 : L.pos[pv] + 1;
+        if (a.depth) a.depth[o + p + 1] = L.dep[win][v];
+        if (a.rank) a.rank[o + p + 1] = (int)(m & 0xffffu);
+      }
+    }
+  } else {
+    if (wave == 0) bt_sequential(lp, lpg, n, a.max_depth, nc, L, lane);
+    __syncthreads();
+    for (int t = tid + 1; t < n; t += kBtWaves * 64) {
+      a.parent[o + t] = L.np_[t];
+      if (a.depth) a.depth[o + t] = L.nd_[t];
+      if (a.rank) a.rank[o + t] = L.nr_[t];
+    }
   }
 }
 
@@ -158,10 +434,10 @@ int launch_build_tree(int B, int n, int max_depth, int n_cand, const double* lp,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (B == 0) return 0;
-  if ((max_depth + 1) * n_cand <= kLpLds)
-    hipLaunchKernelGGL(build_tree<true>, dim3(B), dim3(64), 0, st, a);
+  if ((long long)(max_depth + 1) * n_cand <= kLpLds)
+    hipLaunchKernelGGL(build_tree<true>, dim3(B), dim3(kBtWaves * 64), 0, st, a);
   else
-    hipLaunchKernelGGL(build_tree<false>, dim3(B), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(build_tree<false>, dim3(B), dim3(kBtWaves * 64), 0, st, a);
   return (int)hipGetLastError();
 }
 
