@@ -190,9 +190,11 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
   // ---- page-table slice of this chunk -> LDS
   const int ps = a.kv.page_size;
   int pg0 = 0;
+  bool pt_fits = true;  // every page of the chunk is in the cached slice
   if constexpr (PAGED) {
     pg0 = a.ps_shift >= 0 ? (c0 >> a.ps_shift) : c0 / ps;
     const int pg1 = a.ps_shift >= 0 ? ((c1 - 1) >> a.ps_shift) : (c1 - 1) / ps;
+    pt_fits = pg1 - pg0 < RG::PT_CAP;
     for (int j = tid; j <= pg1 - pg0 && j < RG::PT_CAP; j += 256) {
       const int pg = pg0 + j;
       pt_lds[j] = pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1;
@@ -200,14 +202,21 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
     __syncthreads();
   }
   const long long seq_base = (long long)b * a.kv.seq_stride;
-  auto slot_of = [&](int pos) -> long long {
+  // slot of a position: page entries from the cached slice (FROM_MEM: pages
+  // past it are read from memory; the copy paths keep the two apart, so the
+  // common one never waits on a memory read, which would also wait for every
+  // copy already in flight)
+  auto slot_of = [&](int pos, auto from_mem) -> long long {
     long long s;
     if constexpr (PAGED) {
       const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
-      // pages past the cached slice (a chunk longer than PT_CAP pages) are read from memory
       const int jp = pg - pg0;
-      const int e = jp < RG::PT_CAP ? pt_lds[jp]
-                                : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
+      int e;
+      if constexpr (decltype(from_mem)::value)
+        e = jp < RG::PT_CAP ? pt_lds[jp]
+                            : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
+      else
+        e = pt_lds[jp < RG::PT_CAP ? jp : 0];
       s = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
     } else {
       s = seq_base + pos;
@@ -237,11 +246,18 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
       const char* base = tbase + (seq_base + key0) * slot_bytes;  // wave-uniform
 #pragma unroll
       for (int j = 0; j < RG::LPW; ++j) global_to_lds16(base + dma_off[j], dst + j * 1024);
+    } else if (pt_fits) {
+#pragma unroll
+      for (int j = 0; j < RG::LPW; ++j) {
+        const int pos = key0 + dma_row[j];
+        const long long sl = slot_of(pos < c1 ? pos : c0, std::false_type{});
+        global_to_lds16(tbase + sl * slot_bytes + (dma_off[j] - (int)(dma_row[j] * slot_bytes)), dst + j * 1024);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < RG::LPW; ++j) {
         const int pos = key0 + dma_row[j];
-        const long long sl = pos < c1 ? slot_of(pos) : slot_of(c0);
+        const long long sl = slot_of(pos < c1 ? pos : c0, std::true_type{});
         global_to_lds16(tbase + sl * slot_bytes + (dma_off[j] - (int)(dma_row[j] * slot_bytes)), dst + j * 1024);
       }
     }
@@ -719,11 +735,13 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
   // ---- page-table slice of this chunk -> LDS
   const int ps = a.kv.page_size;
   int pg0 = 0;
+  bool pt_fits = true;  // every page of the chunk is in the cached slice
   if constexpr (PAGED) {
     const int k0 = cblk0 * 32, k1 = min(cblk1 * 32, L);
     if (k1 > k0) {
       pg0 = a.ps_shift >= 0 ? (k0 >> a.ps_shift) : k0 / ps;
       const int pg1 = a.ps_shift >= 0 ? ((k1 - 1) >> a.ps_shift) : (k1 - 1) / ps;
+      pt_fits = pg1 - pg0 < WRg::PT_CAP;
       for (int j = tid; j <= pg1 - pg0 && j < WRg::PT_CAP; j += 256) {
         const int pg = pg0 + j;
         pt_lds[j] = pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1;
@@ -732,14 +750,21 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
     __syncthreads();
   }
   const long long seq_base = (long long)b * a.kv.seq_stride;
-  auto slot_of = [&](int pos) -> long long {
+  // slot of a position: page entries from the cached slice (FROM_MEM: pages
+  // past it are read from memory; the copy paths keep the two apart, so the
+  // common one never waits on a memory read, which would also wait for every
+  // copy already in flight)
+  auto slot_of = [&](int pos, auto from_mem) -> long long {
     long long sl;
     if constexpr (PAGED) {
       const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
-      // pages past the cached slice (a chunk longer than PT_CAP pages) are read from memory
       const int jp = pg - pg0;
-      const int e = jp < WRg::PT_CAP ? pt_lds[jp]
-                                : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
+      int e;
+      if constexpr (decltype(from_mem)::value)
+        e = jp < WRg::PT_CAP ? pt_lds[jp]
+                             : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
+      else
+        e = pt_lds[jp < WRg::PT_CAP ? jp : 0];
       sl = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
     } else {
       sl = seq_base + pos;
@@ -771,11 +796,17 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       const char* bt = tg + (seq_base + key0) * slot_bytes;
 #pragma unroll
       for (int j = 0; j < WRg::LPT; ++j) dma16_sbase(ld + j * 1024, doff[j], bt);
+    } else if (pt_fits) {
+#pragma unroll
+      for (int j = 0; j < WRg::LPT; ++j) {
+        const int pos = key0 + drow[j];
+        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < L ? pos : key0, std::false_type{}) * slot_bytes + dcol[j]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < WRg::LPT; ++j) {
         const int pos = key0 + drow[j];
-        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < L ? pos : key0) * slot_bytes + dcol[j]);
+        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < L ? pos : key0, std::true_type{}) * slot_bytes + dcol[j]);
       }
     }
   };
@@ -1146,10 +1177,12 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   // ---- page-table slice of this chunk -> LDS
   const int ps = a.kv.page_size;
   int pg0 = 0;
+  bool pt_fits = true;  // every page of the chunk is in the cached slice
   if constexpr (PAGED) {
     if (c1 > c0) {
       pg0 = a.ps_shift >= 0 ? (c0 >> a.ps_shift) : c0 / ps;
       const int pg1 = a.ps_shift >= 0 ? ((c1 - 1) >> a.ps_shift) : (c1 - 1) / ps;
+      pt_fits = pg1 - pg0 < RG::PT_CAP;
       for (int j = tid; j <= pg1 - pg0 && j < RG::PT_CAP; j += NT) {
         const int pg = pg0 + j;
         pt_lds[j] = pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1;
@@ -1158,14 +1191,21 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
     __syncthreads();
   }
   const long long seq_base = (long long)b * a.kv.seq_stride;
-  auto slot_of = [&](int pos) -> long long {
+  // slot of a position: page entries from the cached slice (FROM_MEM: pages
+  // past it are read from memory; the copy paths keep the two apart, so the
+  // common one never waits on a memory read, which would also wait for every
+  // copy already in flight)
+  auto slot_of = [&](int pos, auto from_mem) -> long long {
     long long sl;
     if constexpr (PAGED) {
       const int pg = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / ps;
-      // pages past the cached slice (a chunk longer than PT_CAP pages) are read from memory
       const int jp = pg - pg0;
-      const int e = jp < RG::PT_CAP ? pt_lds[jp]
-                                : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
+      int e;
+      if constexpr (decltype(from_mem)::value)
+        e = jp < RG::PT_CAP ? pt_lds[jp]
+                             : (pg < a.kv.max_pages ? a.kv.page_table[(long long)b * a.kv.max_pages + pg] : -1);
+      else
+        e = pt_lds[jp < RG::PT_CAP ? jp : 0];
       sl = e < 0 ? -1 : (long long)e * ps + (pos - pg * ps);
     } else {
       sl = seq_base + pos;
@@ -1190,11 +1230,17 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
       const char* bt = tg + (seq_base + key0) * slot_bytes;
 #pragma unroll
       for (int j = 0; j < LPW; ++j) dma16_sbase(ld + j * 1024, (uint32_t)(drow(j) * slot_bytes) + dcol(j), bt);
+    } else if (pt_fits) {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int pos = key0 + drow(j);
+        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < c1 ? pos : c0, std::false_type{}) * slot_bytes + dcol(j));
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
         const int pos = key0 + drow(j);
-        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < c1 ? pos : c0) * slot_bytes + dcol(j));
+        dma16_vaddr(ld + j * 1024, tg + slot_of(pos < c1 ? pos : c0, std::true_type{}) * slot_bytes + dcol(j));
       }
     }
   };
