@@ -1337,11 +1337,17 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   float* sdst = a.ws_s + ((long long)b * a.Hkv + g) * a.s_stride;
 
   // Stage i: wait for its copies, start the copies of stage i + PD, then the
-  // two blocks' S^T products followed by their softmax and P V.  Stages whose
-  // keys all lie in the prefix need no mask and run a copy of the body
-  // without it (no mask code, no merges of masked and unmasked tiles).
-  auto stage = [&](int i, auto masked) {
+  // two blocks' S^T products, one max and one rescale decision for the
+  // stage's 64 keys, and both blocks' exponentials and P V products in one
+  // branch-free stretch (so the second block's exponentials can issue while
+  // the first block's P V products run on the matrix cores).  The block
+  // scores this wave owns come last, from K fragments read again.  Stages
+  // whose keys all lie in the prefix need no mask and run a copy of the body
+  // without it; stages past the chunk end (the last one of a chunk) skip
+  // their missing blocks.
+  auto stage = [&](int i, auto masked, auto full) {
     constexpr bool MASKED = decltype(masked)::value;
+    constexpr bool FULL = decltype(full)::value;
     // stage i has landed once only the copies of later stages can be outstanding
     const int after = min(RG::PD - 1, n_st - 1 - i);
     if (after >= 2) wait_vm_lgkm0<2 * LPW>();
@@ -1352,49 +1358,31 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
     if (i + RG::PD < n_st) issue(i + RG::PD);
     const char* Kt = smem + (i % RG::NS) * RG::STAGE;
     const char* Vt = Kt + RG::TILE;
+    const int kst = c0 + i * RG::SK;  // first key of the stage
+    const int nb = FULL ? RG::NB : min(RG::NB, (c1 - kst + 31) / 32);
 
     f32x16 sb[RG::NB];
 #pragma unroll
     for (int kb = 0; kb < RG::NB; ++kb) {
-      const int kb0 = c0 + 32 * (i * RG::NB + kb);
-      if (kb0 >= c1) break;
-      const int jblk = kb0 >> 5;
-      const bool do_score = wg_scores && kb0 < Pb && (jblk % a.RB) == rb && ((jblk / a.RB) % NW) == wave;
+      if (!FULL && kb >= nb) break;
       const char* Kb = Kt + kb * 32 * RG::ROWB;
       bf16x8 ka[QN];
 #pragma unroll
       for (int ks = 0; ks < QN; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(Kb + koff[ks]);
       f32x16 s = f32x16{};
-      if (do_score) {
-        f32x16 sc = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < QN; ++ks) {
-          s = mfma_bf16(ka[ks], qf[ks], s);
-          sc = mfma_bf16(ka[ks], *reinterpret_cast<const bf16x8*>(qbt + qb_row * D + 16 * ks + 8 * h), sc);
-        }
-        // columns 0 + 1 + 2 summed by lanes 0 and 32, which hold keys kappa(v, h)
-        float tv[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tv[v] = sc[v] + row_shl<1>(sc[v]) + row_shl<2>(sc[v]);
-        if (lane32 == 0) {  // whole block (rows are padded by 32; entries past P_b are never read)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<f32x4*>(sdst + kb0 + 8 * qd + 4 * h) =
-                f32x4{tv[4 * qd], tv[4 * qd + 1], tv[4 * qd + 2], tv[4 * qd + 3]};
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < QN; ++ks) s = mfma_bf16(ka[ks], qf[ks], s);
-      }
+      for (int ks = 0; ks < QN; ++ks) s = mfma_bf16(ka[ks], qf[ks], s);
       sb[kb] = s;
     }
 
+    // mask (blocks reaching the verify tokens): visible iff j < P_b or j - P_b is
+    // an ancestor-or-self; then the stage max
+    float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < RG::NB; ++kb) {
-      const int kb0 = c0 + 32 * (i * RG::NB + kb);
-      if (kb0 >= c1) break;
+      if (!FULL && kb >= nb) break;
+      const int kb0 = kst + 32 * kb;
       f32x16& s = sb[kb];
-      // mask (blocks reaching the verify tokens): visible iff j < P_b or j - P_b is an ancestor-or-self
       if (MASKED && kb0 + 32 > Pb) {
         if (a.tree) {
           const uint32_t win = anc_window(anc, kb0 - Pb);
@@ -1405,29 +1393,32 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
           for (int v = 0; v < 16; ++v) s[v] = (kb0 + kappa(v, h) - Pb <= t_node) ? s[v] : kNegInf;
         }
       }
-      // online softmax, log2 domain, lazy rescale
-      float mx = s[0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-      mx = half_max(mx) * a.scale_log2;
-      const bool grew = mx > m + kRescaleSlack;
-      if (__any(grew)) {
-        const float mn = grew ? mx : m;
-        const float alpha = grew ? fast_exp2(m - mn) : 1.f;
-        l *= alpha;
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    }
+    // online softmax, log2 domain, lazy rescale (one decision per stage)
+    mx = half_max(mx) * a.scale_log2;
+    const bool grew = mx > m + kRescaleSlack;
+    if (__any(grew)) {
+      const float mn = grew ? mx : m;
+      const float alpha = grew ? fast_exp2(m - mn) : 1.f;
+      l *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        m = mn;
-      }
-      const float mneg = m == kNegInf ? 0.f : -m;
-      float psum = 0.f;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m = mn;
+    }
+    const float mneg = m == kNegInf ? 0.f : -m;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < RG::NB; ++kb) {
+      if (!FULL && kb >= nb) break;
+      f32x16& s = sb[kb];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float p = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, mneg));
         s[v] = p;
         psum += p;
       }
-      l += psum;
       // O^T += V^T P^T
       const char* Vb = Vt + kb * 32 * RG::ROWB;
 #pragma unroll
@@ -1445,10 +1436,42 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
         }
       }
     }
+    l += psum;
+
+    // block scores owned by this wave: scale * k . qbar over columns 0 + 1 + 2
+    // of the score operand, summed by lanes 0 and 32, which hold keys kappa(v, h)
+    if (wg_scores) {
+#pragma unroll
+      for (int kb = 0; kb < RG::NB; ++kb) {
+        if (!FULL && kb >= nb) break;
+        const int kb0 = kst + 32 * kb;
+        const int jblk = kb0 >> 5;
+        if (!(kb0 < Pb && (jblk % a.RB) == rb && ((jblk / a.RB) % NW) == wave)) continue;
+        const char* Kb = Kt + kb * 32 * RG::ROWB;
+        f32x16 sc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < QN; ++ks)
+          sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(Kb + koff[ks]),
+                         *reinterpret_cast<const bf16x8*>(qbt + qb_row * D + 16 * ks + 8 * h), sc);
+        float tv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tv[v] = sc[v] + row_shl<1>(sc[v]) + row_shl<2>(sc[v]);
+        if (lane32 == 0) {  // whole block (rows are padded by 32; entries past P_b are never read)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<f32x4*>(sdst + kb0 + 8 * qd + 4 * h) =
+                f32x4{tv[4 * qd], tv[4 * qd + 1], tv[4 * qd + 2], tv[4 * qd + 3]};
+        }
+      }
+    }
   };
-  const int n_plain = min(max((Pb - c0) / RG::SK, 0), n_st);
-  for (int i = 0; i < n_plain; ++i) stage(i, std::false_type{});
-  for (int i = n_plain; i < n_st; ++i) stage(i, std::true_type{});
+  // stages entirely inside the prefix need no mask; only the last stage of a
+  // chunk can reach past its end
+  const int n_full = (c1 - c0) / RG::SK;
+  const int n_plain = min(max((Pb - c0) / RG::SK, 0), n_full);
+  for (int i = 0; i < n_plain; ++i) stage(i, std::false_type{}, std::true_type{});
+  for (int i = n_plain; i < n_full; ++i) stage(i, std::true_type{}, std::true_type{});
+  if (n_full < n_st) stage(n_full, std::true_type{}, std::false_type{});
 
   // ---- epilogue: this wave's rows are its own -> (m, l, o) partials straight to
   // the workspace (no copy is in flight; the score stores need no wait)
