@@ -292,6 +292,9 @@ def main():
     else:
         roof["kernel"] = "verify_main"
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    # the same launch against the other roof too (the tree workloads sit near the ridge)
+    roof["hbm_frac"] = round(verify_bytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    roof["mfma_frac"] = round(verify_flops / (kern_ms * 1e-3) / 1e12 / peak, 4)
     roof["flops_per_byte"] = round(verify_flops / verify_bytes, 1)
     roof["ridge_flops_per_byte"] = round(ridge, 1)
     roof["algorithmic_bytes"] = verify_bytes

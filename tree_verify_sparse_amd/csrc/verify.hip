@@ -656,13 +656,23 @@ struct WaveRing {
 // wave-uniform base `base` (the scalar-base form of the instruction).  The
 // copies carry the non-temporal hint: K/V is streamed, and the hint took the
 // 32k step from 63.6 to 59.2 us (the 4 x 128k batch from 769 to 697 us).
+// The LDS address (m0) and the scalar base must sit in scalar registers: both
+// are wave-uniform by construction, and readfirstlane says so to the compiler
+// (which otherwise may keep a uniform value in a vector register).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return reinterpret_cast<const void*>(((unsigned long long)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16_sbase(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(off), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(off), "s"(uniform_ptr(base)) : "memory");
 }
 __device__ __forceinline__ void dma16_vaddr(uint32_t lds, const void* addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(addr) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(addr) : "memory");
 }
-
 // s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in {0, step, 2 step, 3 step}
 template <int STEP>
 __device__ __forceinline__ void wait_blocks_after(int blocks) {
@@ -1217,7 +1227,10 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
     return (sl >= 0 && sl < a.kv.num_slots) ? sl : 0;  // unmapped positions read slot 0 (never visible)
   };
 
-  // ---- copies of a stage: segment wave * LPW + j; the first SEGS / 2 segments are K rows, the rest V
+  // ---- copies of a stage: segment wave * LPW + j; the first SEGS / 2 segments are K rows, the rest V.
+  // (The row blocks of a chunk read each tile too; copies without the
+  // non-temporal hint, meant to keep the tiles in L2 for them, measured 4x
+  // slower with 4x the HBM traffic on the 256-node tree.)
   const uint32_t ring_l =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
   const long long slot_bytes = (long long)a.Hkv * RG::ROWB;
@@ -1595,15 +1608,17 @@ __device__ __forceinline__ void merge_select_block(SelShared& L, const VerifyArg
 }
 
 template <typename T, int D, bool OB, bool SEL>
-__global__ void __launch_bounds__(SEL ? 512 : 256) verify_merge(const VerifyArgs a, int n_row_wgs, int wpr) {
+__global__ void __launch_bounds__(SEL ? 512 : 256) verify_merge(const VerifyArgs a, int n_score_wgs, int wpr) {
   constexpr int NT = SEL ? 512 : 256;
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
-  if ((int)blockIdx.x < n_row_wgs) {
+  // the score workgroups come first: they start with the row merges instead
+  // of after all of them (as a tail, on batches with many rows)
+  if ((int)blockIdx.x >= n_score_wgs) {
     __shared__ MergeAcc red[NW][32];
     const int lane = tid & 63, wave = tid >> 6;
     const int sub = wave % wpr;
-    const int gr = (int)blockIdx.x * (NW / wpr) + wave / wpr;  // (b, g, row); uniform over a row's waves
+    const int gr = ((int)blockIdx.x - n_score_wgs) * (NW / wpr) + wave / wpr;  // (b, g, row); uniform over a row's waves
     if (gr >= a.B * a.Hkv * a.R) return;
     const int row = gr % a.R, bg = gr / a.R, g = bg % a.Hkv, b = bg / a.Hkv;
     // every chunk holds a partial (streaming kernel), else the chunks below P_b + N;
@@ -1677,7 +1692,7 @@ __global__ void __launch_bounds__(SEL ? 512 : 256) verify_merge(const VerifyArgs
     }
   } else if constexpr (SEL) {
     __shared__ SelShared L;
-    const int sw = (int)blockIdx.x - n_row_wgs;
+    const int sw = (int)blockIdx.x;
     const int b = sw / kSelMaxBlocks, blk = sw % kSelMaxBlocks;
     if (b >= a.B) return;
     int P, k;
@@ -1686,7 +1701,7 @@ __global__ void __launch_bounds__(SEL ? 512 : 256) verify_merge(const VerifyArgs
     if (sel_blk(P) == 4096) merge_select_block<NT, 4096 / NT, 8>(L, a, b, blk, P, k);
     else merge_select_block<NT, 2048 / NT, 4>(L, a, b, blk, P, k);
   } else {
-    const long long i0 = (long long)(blockIdx.x - n_row_wgs) * 256 + tid;
+    const long long i0 = (long long)blockIdx.x * 256 + tid;
     if (i0 >= (long long)a.B * a.P_max) return;
     const int b = (int)(i0 / a.P_max), i = (int)(i0 % a.P_max);
     int Pb = a.prefix_len[b];
@@ -1953,15 +1968,18 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
   else if (p.RT == 2 && p.WR == 1) launch_main<T, D, 2, 1>(p, a, st, ev0, ev1);
   else if (p.RT == 2 && p.WR == 2) launch_main<T, D, 2, 2>(p, a, st, ev0, ev1);
   else launch_main<T, D, 2, 4>(p, a, st, ev0, ev1);
-  const int wpr = p.n_chunks >= 16 ? 4 : 1;  // waves per merged row
+  // waves per merged row: four when rows are few and long (one sequence's
+  // rows would not fill the GPU otherwise), one when there are many rows
+  const int wpr = (p.n_chunks >= 16 && (long long)p.B * p.Hkv * p.R < 2048) ? 4 : 1;
   const bool ob = p.treek || p.stream;        // the bf16 kernels write their o partials in bf16
   if (a.sel_k) {
     // fused selection: 512-thread workgroups, one per (sequence, selection block)
-    // after the row ones (pass A), then the selection's pass B kernel
+    // (pass A) before the row ones, then the selection's pass B kernel
     const int n_row_wgs = (p.B * p.Hkv * p.R * wpr + 7) / 8;
-    const dim3 grid(n_row_wgs + p.B * kSelMaxBlocks);
-    if (ob) hipLaunchKernelGGL((verify_merge<T, D, true, true>), grid, dim3(512), 0, st, a, n_row_wgs, wpr);
-    else hipLaunchKernelGGL((verify_merge<T, D, false, true>), grid, dim3(512), 0, st, a, n_row_wgs, wpr);
+    const int n_sel = p.B * kSelMaxBlocks;
+    const dim3 grid(n_row_wgs + n_sel);
+    if (ob) hipLaunchKernelGGL((verify_merge<T, D, true, true>), grid, dim3(512), 0, st, a, n_sel, wpr);
+    else hipLaunchKernelGGL((verify_merge<T, D, false, true>), grid, dim3(512), 0, st, a, n_sel, wpr);
     const int e = (int)hipGetLastError();
     if (e) return e;
     return launch_select_pass_b(a.scores, p.B, p.P_max, a.prefix_len, a.sel_k, a.sel_kmax, a.sel_idx, a.sel_count,
@@ -1970,11 +1988,11 @@ static int launch_typed(const VerifyPlan& p, VerifyArgs& a, hipStream_t st, void
   const int n_row_wgs = (p.B * p.Hkv * p.R * wpr + 3) / 4;
   const long long n_s = p.scores ? ((long long)p.B * p.P_max + 255) / 256 : 0;
   if (ob)
-    hipLaunchKernelGGL((verify_merge<T, D, true, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, n_row_wgs,
+    hipLaunchKernelGGL((verify_merge<T, D, true, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, (int)n_s,
                        wpr);
   else
-    hipLaunchKernelGGL((verify_merge<T, D, false, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a,
-                       n_row_wgs, wpr);
+    hipLaunchKernelGGL((verify_merge<T, D, false, false>), dim3(n_row_wgs + (int)n_s), dim3(256), 0, st, a, (int)n_s,
+                       wpr);
   return (int)hipGetLastError();
 }
 
