@@ -84,3 +84,14 @@ def test_fused_ties_take_the_radix_path():
     gi = idx.cpu().numpy()
     for b in range(wl.B):
         assert gi[b, :1000].tolist() == list(range(1000))
+
+
+def test_fused_large_k_fraction():
+    """k a quarter of the row and more (a fixed budget over short contexts):
+    the rows' blocks stay within their slots (1024-entry blocks up to 32768
+    entries), and the selection equals the separate calls' and the oracle band."""
+    wl = make_custom(seed=603, B=4, Hq=8, Hkv=2, D=128, dtype="bf16", P=[8192, 20000, 32768, 6000], N=4,
+                     score_rows="all", k_sel=10, decode_steps=0)
+    k = np.array([2048, 6000, 8192, 3000], np.int32)
+    idx, cnt = _compare(wl, k_sel=k)
+    assert cnt.tolist() == k.tolist()

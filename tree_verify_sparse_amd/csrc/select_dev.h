@@ -4,8 +4,9 @@
 // and by the verify merge kernel, which runs the first pass on the scores it
 // has just summed.
 //
-// A row of P scores is cut into blocks of 2048 entries (4096 for rows longer
-// than 65536, so a row has at most 32 blocks).
+// A row of P scores is cut into blocks of 2048 entries, 4096 for rows longer
+// than 65536 (a row has at most 32 blocks), and 1024 when k is more than an
+// eighth of a row of up to 32768 (a block's share must fit its slots).
 //   Pass A, one workgroup per block: every workgroup of a row computes the
 //     same band [t_lo, t_hi] from the same sample of the row (the k-th largest
 //     entry is expected inside it), and writes its block's entries at or
@@ -80,8 +81,15 @@ __host__ __device__ inline SelWs sel_ws_at(void* base, int B) {
   return w;
 }
 
-// block length of a row: 2048, or 4096 above 65536 entries (at most 32 blocks)
-__host__ __device__ inline int sel_blk(int P) { return P > 65536 ? 4096 : 2048; }
+// block length of a row: 2048 entries up to 65536, 4096 above (at most 32
+// blocks); 1024 for rows up to 32768 whose k is more than an eighth of the row,
+// so that a block's share of the kept entries and the band stays within its
+// 512 slots (with 2048-entry blocks the 8192-entry row at k = 2048 overflowed
+// them and fell back to the radix path; smaller blocks everywhere cost the
+// 32768-entry row 1.6 us)
+__host__ __device__ inline int sel_blk(int P, int k) {
+  return P > 65536 ? 4096 : ((P <= 32768 && 8LL * k > P) ? 1024 : 2048);
+}
 // sample of 2048 entries (4096 for rows above 65536): 256 segments of 8 (16)
 // consecutive entries on 256 threads, nseg segments of sel_seg(P) * 256 / nseg
 __host__ __device__ inline int sel_seg(int P) { return P > 65536 ? 16 : 8; }
@@ -415,7 +423,7 @@ __device__ __forceinline__ void sel_pass_b_row(SelShared& L, const SelWs& ws, in
     sel_radix_row<NT>(L, P, k, k_max, out, count, b, VAL);
     return;
   }
-  const int BL = sel_blk(P);
+  const int BL = sel_blk(P, k);
   const int nb = (P + BL - 1) / BL;
   constexpr int M = kSelMaxBlocks / NW;  // blocks per wave
   constexpr int RR = kSelCap / 64;              // slot rounds per block

@@ -62,10 +62,11 @@ __global__ void __launch_bounds__(kSelThreads) sel_pass_a(const float* __restric
   const int blk = blockIdx.x, b = blockIdx.y;
   int P, k;
   sel_row_sizes(prefix_len, kreq, b, P_max, k_max, &P, &k);
-  if (!sel_multi(P, k) || blk * sel_blk(P) >= P) return;
+  if (!sel_multi(P, k) || blk * sel_blk(P, k) >= P) return;
   const float* s = scores + (long long)b * P_max;
-  if (sel_blk(P) == 4096) sel_pass_a_block<16>(L, s, P, k, b, blk, ws);
-  else sel_pass_a_block<8>(L, s, P, k, b, blk, ws);
+  if (sel_blk(P, k) == 4096) sel_pass_a_block<16>(L, s, P, k, b, blk, ws);
+  else if (sel_blk(P, k) == 2048) sel_pass_a_block<8>(L, s, P, k, b, blk, ws);
+  else sel_pass_a_block<4>(L, s, P, k, b, blk, ws);
 }
 
 // Grid (rows), 1024 threads.
@@ -97,9 +98,10 @@ int launch_topk(const float* scores, int B, int P_max, const int32_t* prefix_len
   if (B <= 0) return 0;
   const SelWs w = sel_ws_at(ws, B);
   if (P_max > kSelMinP) {
-    // the most blocks any row up to P_max has: 2048-entry blocks up to 65536
-    // entries, 4096 above (at most kSelMaxBlocks either way)
-    int nb = (min(P_max, 65536) + 2047) / 2048;
+    // the most blocks any row up to P_max has: 1024-entry blocks up to 32768
+    // entries, 2048 up to 65536, 4096 above (at most kSelMaxBlocks each way)
+    int nb = (min(P_max, 32768) + 1023) / 1024;
+    if (P_max > 32768) nb = max(nb, (min(P_max, 65536) + 2047) / 2048);
     if (P_max > 65536) nb = max(nb, (min(P_max, kSelMaxP) + 4095) / 4096);
     hipLaunchKernelGGL(sel_pass_a, dim3(min(nb, kSelMaxBlocks), B), dim3(kSelThreads), 0, st, scores, P_max,
                        prefix_len, k, k_max, w);

@@ -1533,7 +1533,7 @@ __device__ __forceinline__ MergeAcc merge_acc(const MergeAcc& x, const MergeAcc&
 }
 
 // Fused selection, pass A on the merge's score workgroups (NT threads, one
-// per (sequence, block of sel_blk(P) prefix entries)): the block's scores are
+// per (sequence, block of sel_blk(P, k) prefix entries)): the block's scores are
 // summed from the per-KV-head partials (head order, as every score) and
 // written, then pass A runs on them (band from a sample of summed scores, the
 // block's entries at or above it to the selection workspace).  Pass B is the
@@ -1544,7 +1544,8 @@ __device__ __forceinline__ MergeAcc merge_acc(const MergeAcc& x, const MergeAcc&
 // the partials of all KV heads.
 template <int NT, int E, int SEG>
 __device__ __forceinline__ void merge_select_block(SelShared& L, const VerifyArgs& a, int b, int blk, int P, int k) {
-  static_assert(E % 4 == 0 && SEG % 4 == 0, "16-byte pieces");
+  static_assert(E % 2 == 0 && SEG % 4 == 0, "8- or 16-byte pieces");
+  constexpr int PC = E % 4 == 0 ? 4 : 2;  // floats per block piece
   const int tid = threadIdx.x;
   const int base = blk * E * NT;
   const float* part = a.ws_s + (long long)b * a.Hkv * a.s_stride;  // rows of s_stride (a multiple of 4)
@@ -1562,15 +1563,24 @@ __device__ __forceinline__ void merge_select_block(SelShared& L, const VerifyArg
   // (rows hold P_max + 32 entries, rounded up to whole pieces)
   constexpr int HG = 8;
   for (int g0 = 0; g0 < a.Hkv; g0 += HG) {
-    f32x4 xv[HG][E / 4], sv[HG][SEG / 4];
+    float xv[HG][E];
+    f32x4 sv[HG][SEG / 4];
 #pragma unroll
     for (int j = 0; j < HG; ++j) {
       const bool live = g0 + j < a.Hkv;
       const float* pg = part + (long long)(live ? g0 + j : 0) * a.s_stride;
 #pragma unroll
-      for (int q = 0; q < E / 4; ++q) {
-        const int i = base + E * tid + 4 * q;
-        xv[j][q] = live && i < P ? *reinterpret_cast<const f32x4*>(pg + i) : f32x4{};
+      for (int q = 0; q < E / PC; ++q) {
+        const int i = base + E * tid + PC * q;
+        if constexpr (PC == 4) {
+          const f32x4 v = live && i < P ? *reinterpret_cast<const f32x4*>(pg + i) : f32x4{};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[j][4 * q + e] = v[e];
+        } else {
+          const f32x2 v = live && i < P ? *reinterpret_cast<const f32x2*>(pg + i) : f32x2{};
+          xv[j][2 * q] = v[0];
+          xv[j][2 * q + 1] = v[1];
+        }
       }
 #pragma unroll
       for (int q = 0; q < SEG / 4; ++q)
@@ -1580,9 +1590,7 @@ __device__ __forceinline__ void merge_select_block(SelShared& L, const VerifyArg
     for (int j = 0; j < HG; ++j) {
       if (g0 + j < a.Hkv) {
 #pragma unroll
-        for (int q = 0; q < E / 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * q + e] += xv[j][q][e];
+        for (int e = 0; e < E; ++e) x[e] += xv[j][e];
 #pragma unroll
         for (int q = 0; q < SEG / 4; ++q)
 #pragma unroll
@@ -1697,9 +1705,10 @@ __global__ void __launch_bounds__(SEL ? 512 : 256) verify_merge(const VerifyArgs
     if (b >= a.B) return;
     int P, k;
     sel_row_sizes(a.prefix_len, a.sel_k, b, a.P_max, a.sel_kmax, &P, &k);
-    if (blk * sel_blk(P) >= P) return;
-    if (sel_blk(P) == 4096) merge_select_block<NT, 4096 / NT, 8>(L, a, b, blk, P, k);
-    else merge_select_block<NT, 2048 / NT, 4>(L, a, b, blk, P, k);
+    if (blk * sel_blk(P, k) >= P) return;
+    if (sel_blk(P, k) == 4096) merge_select_block<NT, 4096 / NT, 8>(L, a, b, blk, P, k);
+    else if (sel_blk(P, k) == 2048) merge_select_block<NT, 2048 / NT, 4>(L, a, b, blk, P, k);
+    else merge_select_block<NT, 1024 / NT, 4>(L, a, b, blk, P, k);
   } else {
     const long long i0 = (long long)blockIdx.x * 256 + tid;
     if (i0 >= (long long)a.B * a.P_max) return;
