@@ -178,7 +178,7 @@ struct SelShared {
   uint32_t hist[kSelSampleBins];
   uint32_t cand_key[kSelRankMax];
   int32_t cand_idx[kSelRankMax];
-  uint32_t bsel[kSelMaxBlocks];
+  uint32_t bsel[kSelMaxBlocks];  // kept entries per block, then their offsets
   uint32_t sh[64];   // per-wave partials: [0, 16), [16, 32), [48, 64); scans: [32, 48)
   float mm[32];
   float band[2];
@@ -186,6 +186,7 @@ struct SelShared {
   uint32_t tau_key;  // the cut: order key of tau ...
   int32_t tau_idx;   // ... and i_tie
   uint32_t rq, rab;  // radix path: the digit, the entries above it
+  uint32_t total;    // kept entries of the row
 };
 
 // Exclusive scan of one value per thread over a workgroup of NT threads (one
@@ -411,18 +412,16 @@ __device__ __forceinline__ void sel_radix_row(SelShared& L, int P, int k, int k_
 // l holds slots l, l + 64, ..., of each, so a block's first n slots fill
 // whole slot rounds and empty rounds are skipped).  LD(ptr) performs each
 // 4-byte workspace load; VAL(i) returns entry i of the row (radix path only).
-template <int NT, typename Load, typename Val>
-__device__ __forceinline__ void sel_pass_b_row(SelShared& L, const SelWs& ws, int P, int k, int k_max,
-                                               int32_t* __restrict__ out, int32_t* __restrict__ count, int b,
-                                               Load&& LD, Val&& VAL) {
+// The band path of pass B; false (with nothing written) when the band missed
+// or the threshold bin is crowded, and the caller runs the radix path.
+template <int NT, typename Load>
+__device__ __forceinline__ bool sel_pass_b_band(SelShared& L, const SelWs& ws, int P, int k, int k_max,
+                                                int32_t* __restrict__ out, int32_t* __restrict__ count, int b,
+                                                Load&& LD) {
   static_assert(kSelCap == 64 * 8, "slot geometry");
   constexpr int NW = NT / 64;
   static_assert(NW <= 16 && kSelMaxBlocks % NW == 0, "wave geometry");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (!sel_multi(P, k)) {
-    sel_radix_row<NT>(L, P, k, k_max, out, count, b, VAL);
-    return;
-  }
   const int BL = sel_blk(P, k);
   const int nb = (P + BL - 1) / BL;
   constexpr int M = kSelMaxBlocks / NW;  // blocks per wave
@@ -493,11 +492,7 @@ __device__ __forceinline__ void sel_pass_b_row(SelShared& L, const SelWs& ws, in
     C += L.sh[16 + w];
     over |= L.sh[48 + w];
   }
-  if (over || !(A < (uint32_t)k && A + C >= (uint32_t)k)) {  // the band missed: the exact radix path
-    __syncthreads();
-    sel_radix_row<NT>(L, P, k, k_max, out, count, b, VAL);
-    return;
-  }
+  if (over || !(A < (uint32_t)k && A + C >= (uint32_t)k)) return false;  // the band missed
   // ---- cut: the (k - A)-th largest band entry by (value descending, index
   // ascending): every wave finds the threshold bin itself, its entries are
   // gathered and ranked by one wave
@@ -505,23 +500,33 @@ __device__ __forceinline__ void sel_pass_b_row(SelShared& L, const SelWs& ws, in
   uint32_t ab = 0, Cb = 0;
   const int beta = sel_wave_bin<kBand>(L.hist, kk, &ab, &Cb);
   const uint32_t krem = kk - ab;
-  if (Cb > (uint32_t)kSelRankMax) {  // a crowded bin (many equal scores): the exact radix path
-    __syncthreads();
-    sel_radix_row<NT>(L, P, k, k_max, out, count, b, VAL);
-    return;
-  }
+  if (Cb > (uint32_t)kSelRankMax) return false;  // a crowded bin (many equal scores)
+  // every entry of a bin above the threshold bin (or above the band) is kept:
+  // their number per block, and the threshold bin's entries gathered
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-    if (m < mw)
+  for (int m = 0; m < M; ++m) {
+    if (m < mw) {
+      uint32_t t = 0;
 #pragma unroll
-      for (int r = 0; r < RR; ++r)
-        if (64 * r < nge[m] && in_band(m, r) && bbin(v[m][r]) == beta) {
-          const uint32_t at = atomicAdd(&L.ctr, 1u);
-          L.cand_key[at] = order_key(v[m][r]);
-          L.cand_idx[at] = ix[m][r];
+      for (int r = 0; r < RR; ++r) {
+        if (64 * r < nge[m]) {
+          const bool live = 64 * r + lane < nge[m];
+          t += (uint32_t)__builtin_popcountll(
+              __ballot(live && (v[m][r] > t_hi || (in_band(m, r) && bbin(v[m][r]) > beta))));
+          if (live && in_band(m, r) && bbin(v[m][r]) == beta) {
+            const uint32_t at = atomicAdd(&L.ctr, 1u);
+            L.cand_key[at] = order_key(v[m][r]);
+            L.cand_idx[at] = ix[m][r];
+          }
         }
+      }
+      if (lane == 0) L.bsel[wave + NW * m] = t;
+    }
+  }
   __syncthreads();
-  if (wave == 0) {  // lane j ranks entry j against all Cb (register broadcasts)
+  if (wave == 0) {
+    // lane j ranks entry j of the threshold bin against all Cb (register broadcasts);
+    // the entries ranked below krem are kept
     const bool act = lane < (int)Cb;
     const uint32_t kj = act ? L.cand_key[lane] : 0u;
     const int ij = act ? L.cand_idx[lane] : 0;
@@ -535,34 +540,31 @@ __device__ __forceinline__ void sel_pass_b_row(SelShared& L, const SelWs& ws, in
       L.tau_key = kj;
       L.tau_idx = ij;
     }
+    // block offsets: lane j takes block j's count plus its kept threshold-bin entries
+    uint64_t km = __ballot(act && rank < krem);
+    uint32_t bj = lane < nb ? L.bsel[lane] : 0u;
+    while (km) {
+      const int i = __builtin_ctzll(km);
+      km &= km - 1;
+      bj += (lane < nb && __builtin_amdgcn_readlane(ij, i) / BL == lane) ? 1u : 0u;
+    }
+    const uint32_t binc = sel_wave_scan(bj);
+    if (lane < nb) L.bsel[lane] = binc - bj;
+    if (lane == 63) L.total = binc;
   }
   __syncthreads();
   const float tf = key_value(L.tau_key);
   const int i_tie = L.tau_idx;
+  const uint32_t total = L.total;
   // ---- emit: per block, the kept slots in order at the block's offset
   auto kept = [&](int m, int r) {
     return 64 * r + lane < nge[m] && (v[m][r] > tf || (v[m][r] == tf && ix[m][r] <= i_tie));
   };
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    if (m < mw) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int r = 0; r < RR; ++r)
-        if (64 * r < nge[m]) t += (uint32_t)__builtin_popcountll(__ballot(kept(m, r)));
-      if (lane == 0) L.bsel[wave + NW * m] = t;
-    }
-  }
-  __syncthreads();
-  // block offsets: lane j reads block j's kept count, one wave scan
-  const uint32_t bj = lane < nb ? L.bsel[lane] : 0u;
-  const uint32_t binc = sel_wave_scan(bj);
-  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)binc, 63);
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
     if (m >= mw) break;
     const int j = wave + NW * m;
-    uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)(binc - bj), j);
+    uint32_t pos = L.bsel[j];
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
       if (64 * r >= nge[m]) break;
@@ -576,6 +578,21 @@ __device__ __forceinline__ void sel_pass_b_row(SelShared& L, const SelWs& ws, in
   const int emitted = (int)min(total, (uint32_t)k);
   for (int i = emitted + tid; i < k_max; i += NT) out[i] = -1;
   if (tid == 0 && count) count[b] = emitted;
+  return true;
+}
+
+// Pass B for one row: the band path, or the exact radix path for short rows,
+// k = 0 or P, a missed band and a crowded threshold bin.  The radix path has
+// one call site, after the band path: a pass-B launch executes its code once,
+// so its instruction-cache misses are a large part of its time, and a single,
+// trailing copy of the fallback keeps the common path short and contiguous.
+template <int NT, typename Load, typename Val>
+__device__ __forceinline__ void sel_pass_b_row(SelShared& L, const SelWs& ws, int P, int k, int k_max,
+                                               int32_t* __restrict__ out, int32_t* __restrict__ count, int b,
+                                               Load&& LD, Val&& VAL) {
+  if (sel_multi(P, k) && sel_pass_b_band<NT>(L, ws, P, k, k_max, out, count, b, LD)) return;
+  __syncthreads();  // the band path's LDS is reused
+  sel_radix_row<NT>(L, P, k, k_max, out, count, b, VAL);
 }
 
 }  // namespace sv
