@@ -86,3 +86,34 @@ def test_sink_window_exact():
             ref = oracle.sink_window_select(int(Pb), sink, window)
             assert count[b] == len(ref)
             assert idx[b, : len(ref)].tolist() == ref.tolist() and (idx[b, len(ref):] == -1).all()
+
+
+def _top_nonnan(row, P, k):
+    """The min(k, #finite) largest finite entries of row[:P], lower index first on
+    ties, in increasing index order (the selection's contract for NaN entries)."""
+    s = np.asarray(row[:P], dtype=np.float64)
+    fin = np.nonzero(~np.isnan(s))[0]
+    order = fin[np.lexsort((fin, -s[fin]))]
+    return np.sort(order[:min(k, len(fin))])
+
+
+@pytest.mark.parametrize("P,k,nan_frac", [(3000, 100, 0.3), (30000, 2048, 0.1), (30000, 2048, 0.95),
+                                          (100000, 4096, 0.5), (5000, 4999, 0.01)])
+def test_topk_nan_entries_never_selected(P, k, nan_frac):
+    """Rows holding NaN scores (the band path, the radix path, and rows with
+    fewer finite entries than k): NaN entries are never selected, `count` is the
+    number of indices written, and the rest of the row of indices is -1."""
+    r = np.random.default_rng([P, k, int(nan_frac * 100)])
+    B = 2
+    s = r.standard_normal((B, P)).astype(np.float32)
+    s[r.random((B, P)) < nan_frac] = np.nan
+    st = torch.from_numpy(s).cuda()
+    Pt = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    kt = torch.full((B,), k, dtype=torch.int32, device="cuda")
+    idx, cnt = sv.topk_select(st, Pt, kt, k)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        ref = _top_nonnan(s[b], P, k)
+        assert int(cnt[b]) == len(ref), (b, int(cnt[b]), len(ref))
+        assert np.array_equal(idx[b, :len(ref)], ref), f"row {b}"
+        assert (idx[b, len(ref):] == -1).all()
