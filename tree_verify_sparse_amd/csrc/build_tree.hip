@@ -24,13 +24,19 @@
 //      spaced values below it, later rounds 16 evenly spaced values inside the
 //      bracket found so far;
 //   2. the wave that counted the chosen value holds C = {S >= tau}, which
-//      contains the tree; every node of C gets its place in the order by
-//      counting the nodes before it (equal scores compare parents, walking
-//      up), and the first n - 1 places are numbered 1 .. n - 1.
+//      contains the tree; every node of C gets its place in the order from a
+//      histogram of the scores (the nodes of earlier bins, which all score
+//      higher) plus the nodes of its own bin before it (equal scores compare
+//      parents, walking up), and the first n - 1 places are numbered
+//      1 .. n - 1.
+// A wave stops expanding once a wave with a higher trial value has isolated
+// the tree (the first value reaching n - 1 is then known to be at or below
+// that one), so a round lasts as long as its winner, not its slowest wave.
 // If no trial value isolates at most kBtCap sequences (many exactly equal
 // scores at the threshold), wave 0 runs the sequential expansion instead.
-// No atomics: the result is the same bits on every run, and the same tree as
-// the sequential expansion.
+// The only atomics are LDS integer ones whose order decides nothing (an early-
+// stop flag, a node's slot inside its score bin): the result is the same bits
+// on every run, and the same tree as the sequential expansion.
 #include "select_dev.h"
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -49,7 +55,7 @@ constexpr int kLpLds = 4096;   // log-probabilities kept in LDS when they fit (3
 constexpr int kBtWaves = 16;   // trial thresholds counted at once (one per wave)
 constexpr int kBtCap = 384;    // sequences a wave holds for one trial value
 constexpr int kBtRounds = 8;   // bracketing rounds before the sequential expansion
-constexpr int kBtParts = 4;    // threads counting the places of one node
+constexpr int kBtBins = kBtWaves * 64;  // score bins of the placement (one per thread)
 constexpr uint32_t kBtRoot = 0xffffu;
 
 struct BtShared {
@@ -58,9 +64,10 @@ struct BtShared {
   uint32_t meta[kBtWaves][kBtCap];       // parent's index in the same list << 16 | rank
   uint16_t dep[kBtWaves][kBtCap];        // depth
   int pos[kBtCap];                       // place in the expansion order
-  int part[kBtParts][kBtCap];            // per-slice counts: before | equal << 16
+  int wsum[kBtWaves];                    // per-wave totals of the placement's scan
   int mark[kBtWaves][kBtCap + 64];       // child placement marks
   int cnt[kBtWaves];
+  int done_min;  // the lowest wave whose count already isolates the tree (kBtWaves: none yet)
   double tau[kBtWaves];
   // sequential expansion
   double cum[kMaxNodes];
@@ -75,19 +82,18 @@ __device__ __forceinline__ double next_up(double x) {
 }
 
 // Number of ranks r < nc with sv + row[r] >= tau (a prefix of the sorted
-// list): an 8-way search, each step's probes issued together.
+// list): an 8-way search.  Each step's eight probes are loaded together at
+// clamped places and tested after (a branch around each load made every probe
+// its own trip to LDS).
 __device__ __forceinline__ int bt_count(const double* row, int nc, double sv, double tau) {
   int c = 0;
   for (int span = nc > 64 ? 64 : (nc > 8 ? 8 : 1); span >= 1; span >>= 3) {
-    bool t[8];
+    double x[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = c + span * (k + 1) - 1;
-      t[k] = i < nc && sv + row[i < nc ? i : 0] >= tau;
-    }
+    for (int k = 0; k < 8; ++k) x[k] = row[min(c + span * (k + 1) - 1, nc - 1)];
     int m = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m += t[k] ? 1 : 0;
+    for (int k = 0; k < 8; ++k) m += (c + span * (k + 1) - 1 < nc) & (sv + x[k] >= tau) ? 1 : 0;
     c += span * m;
   }
   return c;
@@ -105,10 +111,12 @@ __device__ __forceinline__ int wave_incl_max(int x) {
 }
 
 // The sequences with score >= tau, level by level, into one wave's lists;
-// their number, or kBtCap + 1 as soon as there would be more than kBtCap.
-// mark: the wave's kBtCap + 64 LDS words for placing children.
+// their number, or kBtCap + 1 as soon as there would be more than kBtCap, or
+// as soon as a wave below this one (a higher trial value) has isolated the
+// tree (*done_min < wave: this wave's count can no longer be the first to
+// reach n - 1).  mark: the wave's kBtCap + 64 LDS words for placing children.
 __device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, double* S, uint32_t* meta,
-                         uint16_t* dep, int* mark, int lane) {
+                         uint16_t* dep, int* mark, const int* done_min, int wave, int lane) {
   int cnt = 0;
   int p0 = -1, np = 1;  // the previous level: first index and size (the root alone at first)
   for (int d = 1; d <= max_depth; ++d) {
@@ -118,7 +126,10 @@ __device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, do
       const int i = base + lane;
       const bool act = i < np;
       const int v = p0 < 0 ? -1 : p0 + i;
-      const double sv = (act && v >= 0) ? S[v] : 0.0;
+      const double s = S[(act && v >= 0) ? v : 0];  // loaded with the flag below
+      const int dm = *done_min;
+      if (dm < wave) return kBtCap + 1;  // wave-uniform
+      const double sv = (act && v >= 0) ? s : 0.0;
       const int c = act ? bt_count(row, nc, sv, tau) : 0;
       const int incl = (int)sel_wave_scan((uint32_t)c);
       const int tot = __builtin_amdgcn_readlane(incl, 63);
@@ -317,6 +328,7 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
     if (a.rank) a.rank[o] = 0;
   }
   if (n <= 1) return;  // the root alone (a uniform exit: no barrier follows)
+  if (tid == 0) L.done_min = kBtWaves;
   __syncthreads();
 
   // 1. bracket the threshold
@@ -334,18 +346,24 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
     } else {
       tau = hi_bad - (hi_bad - lo_ok) * (double)(wave + 1) / (double)(kBtWaves + 1);
     }
-    const int c = bt_expand(lp, nc, a.max_depth, tau, L.S[wave], L.meta[wave], L.dep[wave], L.mark[wave], lane);
+    const int c = bt_expand(lp, nc, a.max_depth, tau, L.S[wave], L.meta[wave], L.dep[wave], L.mark[wave],
+                            &L.done_min, wave, lane);
     if (lane == 0) {
       L.cnt[wave] = c;
       L.tau[wave] = tau;
+      // the waves above this one test lower values: once this count isolates the
+      // tree, theirs are not needed (the first wave reaching n - 1 is at most this one)
+      if (c >= n - 1 && c <= kBtCap) atomicMin(&L.done_min, wave);
     }
     __syncthreads();
+    if (tid == 0) L.done_min = kBtWaves;  // for the next round, which starts after a barrier
+    // the first trial value reaching n - 1 (every count loaded at once)
+    int cj[kBtWaves];
+#pragma unroll
+    for (int j = 0; j < kBtWaves; ++j) cj[j] = L.cnt[j];
     int w = -1;
-    for (int j = 0; j < kBtWaves; ++j)
-      if (L.cnt[j] >= n - 1) {
-        w = j;
-        break;
-      }
+#pragma unroll
+    for (int j = kBtWaves - 1; j >= 0; --j) w = cj[j] >= n - 1 ? j : w;
     if (w >= 0) {
       if (L.cnt[w] <= kBtCap) {
         win = w;
@@ -362,49 +380,49 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
   }
 
   if (win >= 0) {
-    // 2. places in the expansion order; the first n - 1 become nodes 1 .. n - 1
-    const int M = L.cnt[win];
+    // 2. places in the expansion order; the first n - 1 become nodes 1 .. n - 1.
+    // The scores are binned (1024 bins over [tau, hi], one per thread; an
+    // earlier bin means a strictly higher score), a scan of the bin counts
+    // gives every bin its first place, and a node's place is that plus the
+    // nodes of its own bin that come before it.
+    const int M = L.cnt[win];  // <= kBtCap < one node per thread
     const double* S = L.S[win];
     const uint32_t* meta = L.meta[win];
-    // K threads per node, each counting over one slice of the list
-    const int K = min(kBtParts, (kBtWaves * 64) / M);
-    const int span = (M + K - 1) / K;
-    if (tid < K * M) {
-      const int v = tid % M, k = tid / M;
-      const int u0 = k * span, u1 = min(M, u0 + span);
-      const double sv = S[v];
-      int pos = 0, ties = 0;
-      int u = u0;
-      for (; u + 8 <= u1; u += 8) {
-        double x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = S[u + j];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pos += x[j] > sv ? 1 : 0;
-          ties += x[j] == sv ? 1 : 0;
-        }
-      }
-      for (; u < u1; ++u) {
-        const double su = S[u];
-        pos += su > sv ? 1 : 0;
-        ties += su == sv ? 1 : 0;
-      }
-      L.part[k][v] = pos | (ties << 16);
+    int* hist = &L.mark[0][0];     // the child-placement marks are free now
+    int* start = hist + kBtBins;
+    int* bucket = start + kBtBins;
+    const double span = hi - L.tau[win];
+    const double inv = span > 0.0 ? (double)kBtBins / span : 0.0;  // 0: a single bin
+    hist[tid] = 0;
+    __syncthreads();
+    int bv = 0, slot = 0;
+    if (tid < M) {
+      const double x = (hi - S[tid]) * inv;  // >= 0: every score is at most hi
+      bv = x >= (double)(kBtBins - 1) ? kBtBins - 1 : (x > 0.0 ? (int)x : 0);
+      slot = atomicAdd(&hist[bv], 1);  // a place inside the bin (any order: only membership is used)
     }
     __syncthreads();
-    for (int v = tid; v < M; v += kBtWaves * 64) {
-      int pos = 0, ties = 0;
-      for (int k = 0; k < K; ++k) {
-        pos += L.part[k][v] & 0xffff;
-        ties += L.part[k][v] >> 16;
+    {
+      const int h = hist[tid];
+      const int incl = (int)sel_wave_scan((uint32_t)h);
+      if (lane == 63) L.wsum[wave] = incl;
+      __syncthreads();
+      int before = 0;
+#pragma unroll
+      for (int w = 0; w < kBtWaves; ++w) before += w < wave ? L.wsum[w] : 0;
+      start[tid] = before + incl - h;
+    }
+    __syncthreads();
+    if (tid < M) bucket[start[bv] + slot] = tid;
+    __syncthreads();
+    if (tid < M) {
+      const int b0 = start[bv], nb = hist[bv];
+      int pos = b0;
+      for (int j = 0; j < nb; ++j) {
+        const int u = bucket[b0 + j];
+        pos += (u != tid && bt_before(S, meta, u, tid)) ? 1 : 0;
       }
-      if (ties > 1) {  // equal scores (itself included once): the order one level up decides
-        const double sv = S[v];
-        for (int u = 0; u < M; ++u)
-          pos += (u != v && S[u] == sv && bt_before(S, meta, u, v)) ? 1 : 0;
-      }
-      L.pos[v] = pos;
+      L.pos[tid] = pos;
     }
     __syncthreads();
     for (int v = tid; v < M; v += kBtWaves * 64) {
