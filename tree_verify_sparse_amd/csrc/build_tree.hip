@@ -81,17 +81,34 @@ __device__ __forceinline__ double next_up(double x) {
   return __longlong_as_double(x > 0.0 ? u + 1 : u - 1);
 }
 
+// The first step of the search over a depth's sorted list: span and the
+// eight probes (the same for every parent of the level, so loaded once).
+struct BtProbe {
+  int span;
+  double p[8];
+};
+__device__ __forceinline__ BtProbe bt_probe(const double* row, int nc) {
+  BtProbe q;
+  q.span = nc > 64 ? 64 : (nc > 8 ? 8 : 1);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) q.p[k] = row[min(q.span * (k + 1) - 1, nc - 1)];
+  return q;
+}
+
 // Number of ranks r < nc with sv + row[r] >= tau (a prefix of the sorted
-// list): an 8-way search.  Each step's eight probes are loaded together at
-// clamped places and tested after (a branch around each load made every probe
-// its own trip to LDS).
-__device__ __forceinline__ int bt_count(const double* row, int nc, double sv, double tau) {
-  int c = 0;
-  for (int span = nc > 64 ? 64 : (nc > 8 ? 8 : 1); span >= 1; span >>= 3) {
+// list): an 8-way search, the first step from the level's probes, each later
+// step's eight probes loaded together at clamped places and tested after (a
+// branch around each load made every probe its own trip to LDS).
+__device__ __forceinline__ int bt_count(const double* row, int nc, double sv, double tau, const BtProbe& q) {
+  int m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m += (q.span * (k + 1) - 1 < nc) & (sv + q.p[k] >= tau) ? 1 : 0;
+  int c = q.span * m;
+  for (int span = q.span >> 3; span >= 1; span >>= 3) {
     double x[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = row[min(c + span * (k + 1) - 1, nc - 1)];
-    int m = 0;
+    m = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) m += (c + span * (k + 1) - 1 < nc) & (sv + x[k] >= tau) ? 1 : 0;
     c += span * m;
@@ -121,6 +138,12 @@ __device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, do
   int p0 = -1, np = 1;  // the previous level: first index and size (the root alone at first)
   for (int d = 1; d <= max_depth; ++d) {
     const double* row = lp + (long long)d * nc;
+    // the level's constants, loaded once: the search's first probes and the
+    // first four log-probabilities (the children of a parent with few)
+    const BtProbe q = bt_probe(row, nc);
+    double r4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r4[j] = row[min(j, nc - 1)];
     int level = 0;
     for (int base = 0; base < np; base += 64) {
       const int i = base + lane;
@@ -130,17 +153,17 @@ __device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, do
       const int dm = *done_min;
       if (dm < wave) return kBtCap + 1;  // wave-uniform
       const double sv = (act && v >= 0) ? s : 0.0;
-      const int c = act ? bt_count(row, nc, sv, tau) : 0;
+      const int c = act ? bt_count(row, nc, sv, tau, q) : 0;
       const int incl = (int)sel_wave_scan((uint32_t)c);
       const int tot = __builtin_amdgcn_readlane(incl, 63);
       if (cnt + level + tot > kBtCap) return kBtCap + 1;
       const int o = cnt + level + incl - c;  // this lane's first child's place
       const uint32_t pm = (uint32_t)(v < 0 ? kBtRoot : (uint32_t)v) << 16;
       if (wave_max_u32((uint32_t)c) <= 4) {
-        // few children per parent: each lane writes its own (reads issued together)
+        // few children per parent: each lane writes its own
         double ch[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ch[j] = sv + row[j < c ? j : 0];
+        for (int j = 0; j < 4; ++j) ch[j] = sv + r4[j];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (j < c) {
