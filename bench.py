@@ -72,8 +72,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(a sequence's KV heads and chunks would shard across GPUs, each GPU "
+              "running this same path on its share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
