@@ -99,11 +99,24 @@ __global__ void __launch_bounds__(256) sparse_partial(const SparseArgs a) {
   const long long sb = (long long)a.Hkv * ROWB;
   uint4 kx[U], vx[U];
   bool ok[U];
+  long long sl[U];
+  if (a.kv.page_table != nullptr) {
+    // every row's page entry loaded before any is used (a lookup per row in turn
+    // would be one trip to memory each)
+    int ent[U];
+    bool in[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) ent[i] = a.kv.page_table[a.kv.entry_index(b, pos[i], &in[i])];
+#pragma unroll
+    for (int i = 0; i < U; ++i) sl[i] = a.kv.slot_of_entry(pos[i], ent[i], in[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < U; ++i) sl[i] = a.kv.slot(b, pos[i]);
+  }
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     ok[i] = wave * KW + r + RPW * i < nk;
-    long long s = ok[i] ? a.kv.slot(b, pos[i]) : -1;
-    if (s < 0) s = 0;  // rows past the count read slot 0 and are masked below
+    const long long s = (ok[i] && sl[i] >= 0) ? sl[i] : 0;  // rows past the count read slot 0 and are masked below
     kx[i] = *reinterpret_cast<const uint4*>(kb + s * sb);
     vx[i] = *reinterpret_cast<const uint4*>(vb + s * sb);
   }
@@ -317,21 +330,38 @@ __global__ void __launch_bounds__(256) compact_rows(const CompactArgs a) {
   const char* kb = reinterpret_cast<const char*>(a.kv.k);
   const char* vb = reinterpret_cast<const char*>(a.kv.v);
   for (int base = 0; base < total; base += 256 * U) {
-    // loads at clamped (always valid) pieces, all issued before the first store
+    // loads at clamped (always valid) pieces, all issued before the first store;
+    // positions, then page entries, then rows, each step's loads issued together
     u32x4 kx[U], vx[U];
-    long long dst[U];
+    long long dst[U], sl[U];
+    int pos[U], cc[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = base + tid + 256 * u;
       ok[u] = e < total;
       const int ec = ok[u] ? e : total - 1;
-      const int r = ec / a.row_pieces, c = ec % a.row_pieces;
-      long long sl = a.kv.slot(b, a.idx[(long long)b * a.idx_stride + j0 + r]);
-      if (sl < 0) sl = 0;  // unmapped positions copy slot 0 (a caller-contract violation)
-      dst[u] = ((long long)b * a.cap + j0 + r) * row_bytes + c * 16;
-      kx[u] = *reinterpret_cast<const u32x4*>(kb + sl * row_bytes + c * 16);
-      vx[u] = *reinterpret_cast<const u32x4*>(vb + sl * row_bytes + c * 16);
+      const int r = ec / a.row_pieces;
+      cc[u] = ec % a.row_pieces;
+      pos[u] = a.idx[(long long)b * a.idx_stride + j0 + r];
+      dst[u] = ((long long)b * a.cap + j0 + r) * row_bytes + cc[u] * 16;
+    }
+    if (a.kv.page_table != nullptr) {
+      int ent[U];
+      bool in[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) ent[u] = a.kv.page_table[a.kv.entry_index(b, pos[u], &in[u])];
+#pragma unroll
+      for (int u = 0; u < U; ++u) sl[u] = a.kv.slot_of_entry(pos[u], ent[u], in[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) sl[u] = a.kv.slot(b, pos[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long s = sl[u] >= 0 ? sl[u] : 0;  // unmapped positions copy slot 0 (a caller-contract violation)
+      kx[u] = *reinterpret_cast<const u32x4*>(kb + s * row_bytes + cc[u] * 16);
+      vx[u] = *reinterpret_cast<const u32x4*>(vb + s * row_bytes + cc[u] * 16);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -145,12 +145,23 @@ struct KvView {
     if (page_table == nullptr) {
       s = (long long)b * seq_stride + pos;
     } else {
-      int pg = pos / page_size;
-      if (pg < 0 || pg >= max_pages) return -1;
-      int phys = page_table[(long long)b * max_pages + pg];
-      s = (long long)phys * page_size + (pos - pg * page_size);
+      bool in;
+      s = slot_of_entry(pos, page_table[entry_index(b, pos, &in)], in);
     }
     return (s >= 0 && s < num_slots && pos >= 0) ? s : -1;
+  }
+  // Paged caches, in two steps, so that a caller can issue the page-table loads
+  // of several positions before it uses any (one trip to memory for all of them,
+  // not one each): the table entry of a position (clamped into the table; *in
+  // says whether the page exists), then the slot from that entry.
+  __device__ __forceinline__ long long entry_index(int b, int pos, bool* in) const {
+    const int pg = pos / page_size;
+    *in = pos >= 0 && pg < max_pages;
+    return (long long)b * max_pages + (*in ? pg : 0);
+  }
+  __device__ __forceinline__ long long slot_of_entry(int pos, int entry, bool in) const {
+    const long long s = (long long)entry * page_size + (pos - (pos / page_size) * page_size);
+    return (in && entry >= 0 && s < num_slots) ? s : -1;
   }
 };
 
