@@ -300,8 +300,15 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
       for (int d = tid; d < D; d += 256) {
         const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
         float acc = 0.f;
-#pragma unroll 16
-        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];  // unrolled: the loads go out together
+        for (int sp0 = 0; sp0 < a.qsplit; sp0 += 16) {
+          // sixteen loads at clamped places issued together, then summed in order (a
+          // bounded loop's load per step would be one trip to memory each)
+          float x[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) x[u] = part[min(sp0 + u, a.qsplit - 1) * D];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) acc += sp0 + u < a.qsplit ? x[u] : 0.f;
+        }
         qs[d] = acc;
       }
     } else {
@@ -309,10 +316,20 @@ __global__ void __launch_bounds__(256) verify_main(const VerifyArgs a) {
       const int d = tid % D, part = tid / D;
       const int npairs = a.n_score_rows * a.G;
       float acc = 0.f;
-      for (int i = part; i < npairs; i += NP) {
-        const int t = a.score_rows[i / a.G], j = i % a.G;
-        const T* qrow = reinterpret_cast<const T*>(a.q) + ((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D;
-        acc += (float)qrow[d];
+      for (int i0 = part; i0 < npairs; i0 += 8 * NP) {
+        // eight pairs at a time: their row indices, then their query elements, each
+        // step's loads issued together at clamped places, then summed in order
+        int t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = a.score_rows[min(i0 + u * NP, npairs - 1) / a.G];
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(i0 + u * NP, npairs - 1) % a.G;
+          x[u] = (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t[u]) * a.Hq + g * a.G + j) * D + d];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += i0 + u * NP < npairs ? x[u] : 0.f;
       }
       qs[D + part * D + d] = acc;
       __syncthreads();
@@ -852,8 +869,15 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       for (int d = tid; d < D; d += 256) {
         const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
         float acc = 0.f;
-#pragma unroll 16
-        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];  // unrolled: the loads go out together
+        for (int sp0 = 0; sp0 < a.qsplit; sp0 += 16) {
+          // sixteen loads at clamped places issued together, then summed in order (a
+          // bounded loop's load per step would be one trip to memory each)
+          float x[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) x[u] = part[min(sp0 + u, a.qsplit - 1) * D];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) acc += sp0 + u < a.qsplit ? x[u] : 0.f;
+        }
         qs[d] = acc;
       }
     } else {
@@ -861,10 +885,20 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       const int d = tid % D, part = tid / D;
       const int npairs = a.n_score_rows * a.G;
       float acc = 0.f;
-#pragma unroll 4
-      for (int i = part; i < npairs; i += NP) {
-        const int t = a.score_rows[i / a.G], j = i % a.G;
-        acc += (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + d];
+      for (int i0 = part; i0 < npairs; i0 += 8 * NP) {
+        // eight pairs at a time: their row indices, then their query elements, each
+        // step's loads issued together at clamped places, then summed in order
+        int t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = a.score_rows[min(i0 + u * NP, npairs - 1) / a.G];
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(i0 + u * NP, npairs - 1) % a.G;
+          x[u] = (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t[u]) * a.Hq + g * a.G + j) * D + d];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += i0 + u * NP < npairs ? x[u] : 0.f;
       }
       qs[D + part * D + d] = acc;
       __syncthreads();
@@ -900,10 +934,12 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int w = 0; w < kAncWords; ++w) {
-        anc[rt][w] = a.ws_anc[((long long)b * a.N + row_node[rt]) * kAncWords + w];
-        asm volatile("" ::"v"(anc[rt][w]));  // wait for the load here, not inside the loop
-      }
+      for (int w = 0; w < kAncWords; ++w) anc[rt][w] = a.ws_anc[((long long)b * a.N + row_node[rt]) * kAncWords + w];
+    // wait for the words here (all loads in flight together), not inside the loop
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      asm volatile("" ::"v"(anc[rt][0]), "v"(anc[rt][1]), "v"(anc[rt][2]), "v"(anc[rt][3]), "v"(anc[rt][4]),
+                   "v"(anc[rt][5]), "v"(anc[rt][6]), "v"(anc[rt][7]));
   }
 
   // ---- per-lane LDS offsets of the operand reads inside a block
@@ -1293,8 +1329,15 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
       for (int d = tid; d < D; d += NT) {
         const float* part = a.ws_qbar + (long long)(b * a.Hkv + g) * a.qsplit * D + d;
         float acc = 0.f;
-#pragma unroll 16
-        for (int sp = 0; sp < a.qsplit; ++sp) acc += part[sp * D];  // unrolled: the loads go out together
+        for (int sp0 = 0; sp0 < a.qsplit; sp0 += 16) {
+          // sixteen loads at clamped places issued together, then summed in order (a
+          // bounded loop's load per step would be one trip to memory each)
+          float x[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) x[u] = part[min(sp0 + u, a.qsplit - 1) * D];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) acc += sp0 + u < a.qsplit ? x[u] : 0.f;
+        }
         qs[d] = acc;
       }
     } else {
@@ -1302,10 +1345,20 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
       const int d = tid % D, part = tid / D;
       const int npairs = a.n_score_rows * a.G;
       float acc = 0.f;
-#pragma unroll 4
-      for (int i = part; i < npairs; i += NP) {
-        const int t = a.score_rows[i / a.G], j = i % a.G;
-        acc += (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t) * a.Hq + g * a.G + j) * D + d];
+      for (int i0 = part; i0 < npairs; i0 += 8 * NP) {
+        // eight pairs at a time: their row indices, then their query elements, each
+        // step's loads issued together at clamped places, then summed in order
+        int t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = a.score_rows[min(i0 + u * NP, npairs - 1) / a.G];
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(i0 + u * NP, npairs - 1) % a.G;
+          x[u] = (float)reinterpret_cast<const T*>(a.q)[((long long)(b * a.N + t[u]) * a.Hq + g * a.G + j) * D + d];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += i0 + u * NP < npairs ? x[u] : 0.f;
       }
       qs[D + part * D + d] = acc;
       __syncthreads();
@@ -1330,8 +1383,8 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   }
 
   if (need_anc) {
-#pragma unroll
-    for (int w = 0; w < kAncWords; ++w) asm volatile("" ::"v"(anc[w]));  // wait for the loads here, not inside the loop
+    asm volatile("" ::"v"(anc[0]), "v"(anc[1]), "v"(anc[2]), "v"(anc[3]), "v"(anc[4]), "v"(anc[5]), "v"(anc[6]),
+                 "v"(anc[7]));  // wait for the loads here (all in flight together), not inside the loop
   }
 
   // ---- per-lane LDS offsets of the operand reads inside a 32-key block
