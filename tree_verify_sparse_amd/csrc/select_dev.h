@@ -126,6 +126,22 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
+// hist[bin] += 1 for every lane of the wave with `hit`.  When all of them hold
+// the same bin (rows of equal scores), one lane adds their number: a whole
+// wave's atomics on one LDS address are serialized, and the fallback that rows
+// of equal scores take would otherwise spend most of its time there.
+__device__ __forceinline__ void sel_hist_add(uint32_t* hist, uint32_t bin, bool hit) {
+  const unsigned long long hm = __ballot(hit);
+  if (hm == 0ull) return;
+  const int first = __builtin_ctzll(hm);
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+  if (__ballot(hit && bin == b0) == hm) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[b0], (uint32_t)__builtin_popcountll(hm));
+  } else if (hit) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
 // Inclusive scan over the 64 lanes of a wave (DPP row shifts, then row broadcasts).
 __device__ __forceinline__ uint32_t sel_wave_scan(uint32_t x) {
   x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);
@@ -343,11 +359,16 @@ __device__ __forceinline__ void sel_radix_row(SelShared& L, int P, int k, int k_
   for (int d = 3; d >= 0; --d) {
     for (int i = tid; i < 256; i += NT) L.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < P; i += NT) {
-      const float x = VAL(i);
-      if (x == x) {
-        const uint32_t key = order_key(x);
-        if ((key & pmask) == prefix) atomicAdd(&L.hist[(key >> (8 * d)) & 255u], 1u);
+    for (int i0 = tid; i0 < P; i0 += 8 * NT) {
+      // eight entries per thread loaded together at clamped places, then counted
+      // (one entry per step would be one trip to memory each)
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = VAL(min(i0 + u * NT, P - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t key = order_key(x[u]);
+        sel_hist_add(L.hist, (key >> (8 * d)) & 255u, i0 + u * NT < P && x[u] == x[u] && (key & pmask) == prefix);
       }
     }
     __syncthreads();
@@ -377,11 +398,17 @@ __device__ __forceinline__ void sel_radix_row(SelShared& L, int P, int k, int k_
   // thread t's run [r0, r1): entries above tau, entries equal to it
   const int r0 = (int)((long long)tid * P / NT), r1 = (int)((long long)(tid + 1) * P / NT);
   uint32_t gt = 0, eq = 0;
-  for (int i = r0; i < r1; ++i) {
-    const float x = VAL(i);
-    const uint32_t key = order_key(x);
-    gt += (x == x && key > prefix) ? 1u : 0u;
-    eq += (x == x && key == prefix && !all_valid) ? 1u : 0u;
+  for (int i0 = r0; i0 < r1; i0 += 8) {  // loads in batches of eight, as above
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = VAL(min(i0 + u, r1 - 1));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t key = order_key(x[u]);
+      const bool in = i0 + u < r1 && x[u] == x[u];
+      gt += (in && key > prefix) ? 1u : 0u;
+      eq += (in && key == prefix && !all_valid) ? 1u : 0u;
+    }
   }
   uint32_t tot;
   const uint32_t eq_before = sel_block_scan<NT>(L, eq, &tot);
@@ -390,17 +417,23 @@ __device__ __forceinline__ void sel_radix_row(SelShared& L, int P, int k, int k_
   uint32_t kept_total;
   uint32_t pos = sel_block_scan<NT>(L, gt + take, &kept_total);
   uint32_t eq_seen = eq_before;
-  for (int i = r0; i < r1; ++i) {
-    const float x = VAL(i);
-    const uint32_t key = order_key(x);
-    bool keep = x == x && key > prefix;
-    if (x == x && key == prefix && !all_valid) {
-      keep = eq_seen < need;
-      ++eq_seen;
-    }
-    if (keep) {
-      if (pos < (uint32_t)k) out[pos] = i;
-      ++pos;
+  for (int i0 = r0; i0 < r1; i0 += 8) {  // in index order, loads in batches of eight
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = VAL(min(i0 + u, r1 - 1));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u >= r1) break;
+      const uint32_t key = order_key(x[u]);
+      bool keep = x[u] == x[u] && key > prefix;
+      if (x[u] == x[u] && key == prefix && !all_valid) {
+        keep = eq_seen < need;
+        ++eq_seen;
+      }
+      if (keep) {
+        if (pos < (uint32_t)k) out[pos] = i0 + u;
+        ++pos;
+      }
     }
   }
   const int emitted = (int)min(kept_total, (uint32_t)k);
