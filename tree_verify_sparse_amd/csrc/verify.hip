@@ -1769,14 +1769,27 @@ __global__ void __launch_bounds__(SEL ? 512 : 256) verify_merge(const VerifyArgs
     int Pb = a.prefix_len[b];
     Pb = Pb < 0 ? 0 : (Pb > a.P_max ? a.P_max : Pb);
     if (i >= Pb) return;
+    // the KV heads' partials eight at a time, loaded together at clamped places
+    // (a load per step of a bounded loop would be one trip to memory each)
     if (a.head_scores) {  // each KV head's own sum over its query heads and the scoring rows
-      for (int g = 0; g < a.Hkv; ++g)
-        a.scores[((long long)b * a.Hkv + g) * a.P_max + i] = a.ws_s[((long long)b * a.Hkv + g) * a.s_stride + i];
+      for (int g0 = 0; g0 < a.Hkv; g0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = a.ws_s[((long long)b * a.Hkv + min(g0 + u, a.Hkv - 1)) * a.s_stride + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (g0 + u < a.Hkv) a.scores[((long long)b * a.Hkv + g0 + u) * a.P_max + i] = x[u];
+      }
       return;
     }
-    float s = 0.f;
-#pragma unroll 8
-    for (int g = 0; g < a.Hkv; ++g) s += a.ws_s[((long long)b * a.Hkv + g) * a.s_stride + i];
+    float s = 0.f;  // summed in head order
+    for (int g0 = 0; g0 < a.Hkv; g0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = a.ws_s[((long long)b * a.Hkv + min(g0 + u, a.Hkv - 1)) * a.s_stride + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += g0 + u < a.Hkv ? x[u] : 0.f;
+    }
     a.scores[i0] = s;
   }
 }
