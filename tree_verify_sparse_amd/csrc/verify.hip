@@ -837,10 +837,13 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       }
     }
   };
+  // the first block's copies, then the query loads, then the other ring slot's
+  // copies: the query fragments arrive ahead of the second block (measured 0.6 us
+  // faster at 32k than both blocks first)
   const int nb = blk1 - blk0;
-  for (int i = 0; i < WRg::NSW && i < nb; ++i) {
-    issue(blk0 + i, i, false);
-    issue(blk0 + i, i, true);
+  if (nb > 0) {
+    issue(blk0, 0, false);
+    issue(blk0, 0, true);
   }
 
   // ---- query fragments (B operand of S^T = K Q^T): lane column = query row
@@ -859,6 +862,11 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * h);
       qf[rt][ks] = ok ? x : bf16x8{};
     }
+  }
+
+  for (int i = 1; i < WRg::NSW && i < nb; ++i) {
+    issue(blk0 + i, i, false);
+    issue(blk0 + i, i, true);
   }
 
   // ---- score operand: scale * qbar_g split into bf16 hi + mid + lo = B columns 0..2
