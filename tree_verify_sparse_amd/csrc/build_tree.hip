@@ -20,9 +20,10 @@
 //      counting, in each of the 16 waves, the sequences at or above one trial
 //      value (level by level: a node at depth d - 1 with score s has exactly
 //      the children r with s + lp[d][r] >= tau, a prefix of the sorted list);
-//      the first round tries the best depth-1 score and 15 geometrically
-//      spaced values below it, later rounds 16 evenly spaced values inside the
-//      bracket found so far;
+//      the first round tries 16 values from 0.4 to 1.67 times the spread of
+//      the depth-1 list below the best depth-1 score (10% apart), later rounds
+//      16 evenly spaced values inside the bracket found so far, or values
+//      spaced ever wider below the lowest one tried;
 //   2. the wave that counted the chosen value holds C = {S >= tau}, which
 //      contains the tree; every node of C gets its place in the order from a
 //      histogram of the scores (the nodes of earlier bins, which all score
@@ -360,12 +361,24 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
   double hi_bad = next_up(hi);       // fewer than n - 1 at or above it (none above hi)
   double geo = 0.125;
   int win = -1;
+  // scale of the first round: the spread of the depth-1 list over its first
+  // min(n_cand, n) ranks (the answer's distance below hi is of that order)
+  const double spread = hi - lp[1 * nc + min(nc, n) - 1];
+  const bool scaled = spread > 0.0 && spread < 1e300;
   for (int rnd = 0; rnd < kBtRounds && win < 0; ++rnd) {
     double tau;
-    if (lo_ok == -__builtin_inf()) {
+    if (rnd == 0 && scaled) {
+      double o = 0.4 * spread;  // 0.4 .. 1.67 spreads below hi, 10% apart
+      for (int w = 0; w < wave; ++w) o *= 1.1;
+      tau = hi - o;
+    } else if (rnd == 0) {
       double g = geo;
       for (int w = 1; w < wave; ++w) g *= 1.6;
       tau = wave == 0 ? hi : hi - g;
+    } else if (lo_ok == -__builtin_inf()) {
+      double g = geo;
+      for (int w = 0; w < wave; ++w) g *= 1.6;
+      tau = hi_bad - g;  // below every value known to isolate fewer than n - 1
     } else {
       tau = hi_bad - (hi_bad - lo_ok) * (double)(wave + 1) / (double)(kBtWaves + 1);
     }
@@ -394,10 +407,10 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
         lo_ok = L.tau[w];
         if (w > 0) hi_bad = L.tau[w - 1];
       }
-    } else if (lo_ok == -__builtin_inf()) {
-      for (int j = 0; j < kBtWaves; ++j) geo *= 1.6;
     } else {
-      hi_bad = L.tau[kBtWaves - 1];
+      hi_bad = L.tau[kBtWaves - 1];  // every value tested isolates fewer than n - 1
+      if (lo_ok == -__builtin_inf() && !(rnd == 0 && scaled))
+        for (int j = 0; j < kBtWaves; ++j) geo *= 1.6;
     }
     if (win < 0) __syncthreads();  // the lists are rewritten by the next round
   }
