@@ -54,7 +54,7 @@ struct BuildArgs {
 
 constexpr int kLpLds = 4096;   // log-probabilities kept in LDS when they fit (32 KB)
 constexpr int kBtWaves = 16;   // trial thresholds counted at once (one per wave)
-constexpr int kBtCap = 384;    // sequences a wave holds for one trial value
+constexpr int kBtCap = 512;    // sequences a wave holds for one trial value
 constexpr int kBtRounds = 8;   // bracketing rounds before the sequential expansion
 constexpr int kBtBins = kBtWaves * 64;  // score bins of the placement (one per thread)
 constexpr uint32_t kBtRoot = 0xffffu;
@@ -62,11 +62,10 @@ constexpr uint32_t kBtRoot = 0xffffu;
 struct BtShared {
   double lp[kLpLds];
   double S[kBtWaves][kBtCap];            // scores
-  uint32_t meta[kBtWaves][kBtCap];       // parent's index in the same list << 16 | rank
-  uint16_t dep[kBtWaves][kBtCap];        // depth
+  uint32_t meta[kBtWaves][kBtCap];       // parent's index in the same list << 16 | rank << 8 | depth
   int pos[kBtCap];                       // place in the expansion order
   int wsum[kBtWaves];                    // per-wave totals of the placement's scan
-  int mark[kBtWaves][kBtCap + 64];       // child placement marks
+  int8_t mark[kBtWaves][kBtCap + 64];    // child placement marks (lane numbers)
   int cnt[kBtWaves];
   int done_min;  // the lowest wave whose count already isolates the tree (kBtWaves: none yet)
   double tau[kBtWaves];
@@ -132,9 +131,9 @@ __device__ __forceinline__ int wave_incl_max(int x) {
 // their number, or kBtCap + 1 as soon as there would be more than kBtCap, or
 // as soon as a wave below this one (a higher trial value) has isolated the
 // tree (*done_min < wave: this wave's count can no longer be the first to
-// reach n - 1).  mark: the wave's kBtCap + 64 LDS words for placing children.
+// reach n - 1).  mark: the wave's kBtCap + 64 LDS bytes for placing children.
 __device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, double* S, uint32_t* meta,
-                         uint16_t* dep, int* mark, const int* done_min, int wave, int lane) {
+                         int8_t* mark, const int* done_min, int wave, int lane) {
   int cnt = 0;
   int p0 = -1, np = 1;  // the previous level: first index and size (the root alone at first)
   for (int d = 1; d <= max_depth; ++d) {
@@ -169,21 +168,20 @@ __device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, do
         for (int j = 0; j < 4; ++j)
           if (j < c) {
             S[o + j] = ch[j];
-            meta[o + j] = pm | (uint32_t)j;
-            dep[o + j] = (uint16_t)d;
+            meta[o + j] = pm | (uint32_t)j << 8 | (uint32_t)d;
           }
       } else {
         // children in lane order: lane l's occupy [incl_l - c_l, incl_l) of
         // this batch.  Each parent marks its first child's place; an
         // inclusive max over the marks gives every place its parent lane.
-        for (int t = lane; t < tot; t += 64) mark[t] = -1;
+        for (int t = lane; t < tot; t += 64) mark[t] = (int8_t)-1;
         __builtin_amdgcn_wave_barrier();
-        if (c > 0) mark[incl - c] = lane;
+        if (c > 0) mark[incl - c] = (int8_t)lane;
         __builtin_amdgcn_wave_barrier();
         int carry = -1;
         for (int t0 = 0; t0 < tot; t0 += 64) {
           const int t = t0 + lane;
-          int pl = wave_incl_max(t < tot ? mark[t] : -1);
+          int pl = wave_incl_max(t < tot ? (int)mark[t] : -1);
           pl = max(pl, carry);  // every place below tot has a parent; lanes past it read lane 0
           carry = __builtin_amdgcn_readlane(pl, 63);
           pl = max(pl, 0);
@@ -195,8 +193,7 @@ __device__ int bt_expand(const double* lp, int nc, int max_depth, double tau, do
             const int r = t - pfirst;
             const int w = cnt + level + t;
             S[w] = psv + row[r];
-            meta[w] = (uint32_t)(pv < 0 ? kBtRoot : (uint32_t)pv) << 16 | (uint32_t)r;
-            dep[w] = (uint16_t)d;
+            meta[w] = (uint32_t)(pv < 0 ? kBtRoot : (uint32_t)pv) << 16 | (uint32_t)r << 8 | (uint32_t)d;
           }
         }
       }
@@ -222,7 +219,7 @@ __device__ __forceinline__ bool bt_before(const double* S, const uint32_t* meta,
     if (su != sv) return su > sv;
     const uint32_t mu = meta[u], mv = meta[v];
     const uint32_t pu = mu >> 16, pv = mv >> 16;
-    if (pu == pv) return (mu & 0xffffu) < (mv & 0xffffu);
+    if (pu == pv) return ((mu >> 8) & 0xffu) < ((mv >> 8) & 0xffu);
     if (pu == kBtRoot) return true;
     if (pv == kBtRoot) return false;
     u = (int)pu;
@@ -382,7 +379,7 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
     } else {
       tau = hi_bad - (hi_bad - lo_ok) * (double)(wave + 1) / (double)(kBtWaves + 1);
     }
-    const int c = bt_expand(lp, nc, a.max_depth, tau, L.S[wave], L.meta[wave], L.dep[wave], L.mark[wave],
+    const int c = bt_expand(lp, nc, a.max_depth, tau, L.S[wave], L.meta[wave], L.mark[wave],
                             &L.done_min, wave, lane);
     if (lane == 0) {
       L.cnt[wave] = c;
@@ -424,9 +421,11 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
     const int M = L.cnt[win];  // <= kBtCap < one node per thread
     const double* S = L.S[win];
     const uint32_t* meta = L.meta[win];
-    int* hist = &L.mark[0][0];     // the child-placement marks are free now
-    int* start = hist + kBtBins;
-    int* bucket = start + kBtBins;
+    // the other waves' score lists are free now
+    static_assert(kBtCap * sizeof(double) >= kBtBins * sizeof(int), "a list holds a histogram");
+    int* hist = reinterpret_cast<int*>(L.S[(win + 1) % kBtWaves]);
+    int* start = reinterpret_cast<int*>(L.S[(win + 2) % kBtWaves]);
+    int* bucket = reinterpret_cast<int*>(L.S[(win + 3) % kBtWaves]);
     const double span = hi - L.tau[win];
     const double inv = span > 0.0 ? (double)kBtBins / span : 0.0;  // 0: a single bin
     hist[tid] = 0;
@@ -467,8 +466,8 @@ __global__ void __launch_bounds__(kBtWaves * 64) build_tree(const BuildArgs a) {
         const uint32_t m = meta[v];
         const uint32_t pv = m >> 16;
         a.parent[o + p + 1] = pv == kBtRoot ? 0 : L.pos[pv] + 1;
-        if (a.depth) a.depth[o + p + 1] = L.dep[win][v];
-        if (a.rank) a.rank[o + p + 1] = (int)(m & 0xffffu);
+        if (a.depth) a.depth[o + p + 1] = (int)(m & 0xffu);
+        if (a.rank) a.rank[o + p + 1] = (int)((m >> 8) & 0xffu);
       }
     }
   } else {
