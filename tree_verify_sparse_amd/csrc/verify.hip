@@ -1619,10 +1619,12 @@ __device__ __forceinline__ void merge_select_block(SelShared& L, const VerifyArg
   for (int e = 0; e < E; ++e) x[e] = 0.f;
 #pragma unroll
   for (int e = 0; e < SEG; ++e) smp[e] = 0.f;
-  // every load of a group of 8 KV heads before its sums (in head order, as
+  // every load of a group of KV heads before its sums (in head order, as
   // every score is formed); a piece starting below P_b ends inside the row
-  // (rows hold P_max + 32 entries, rounded up to whole pieces)
-  constexpr int HG = 8;
+  // (rows hold P_max + 32 entries, rounded up to whole pieces).  Groups hold at
+  // most 64 values in flight per thread (8 heads, or 4 for 8-entry pieces), so
+  // the kernel's row merges keep their occupancy.
+  constexpr int HG = (E + SEG) * 8 > 64 ? 4 : 8;
   for (int g0 = 0; g0 < a.Hkv; g0 += HG) {
     float xv[HG][E];
     f32x4 sv[HG][SEG / 4];
