@@ -90,3 +90,23 @@ def test_build_tree_random_shapes(kind):
             lps.append(lp)
         print(f"[case] {kind} #{t}: B={B} n={n} depth={depth} n_cand={nc}", flush=True)
         _check(np.stack(lps), n, depth)
+
+
+def test_build_tree_many_large_budgets():
+    """Budgets near the 256-node maximum over deep and wide candidate lists
+    (up to depth 12 and 64 candidates), with a few exact-tie grids mixed in: the
+    trial values then isolate several hundred sequences, near the per-wave list
+    limit, and the first round's spacing is exercised on many list shapes."""
+    r = np.random.default_rng(777)
+    for t in range(60):
+        depth = int(r.integers(3, 13))
+        nc = int(r.integers(8, 65))
+        n = int(r.integers(128, 257))
+        lp = depth_logprobs(r, depth, n_cand=nc, var=float(r.uniform(0.5, 4.0)))
+        grid = t % 4
+        if grid == 1:
+            lp = np.round(lp * 16) / 16
+        elif grid == 2:
+            lp = lp * float(r.uniform(0.05, 0.3))  # scores packed close together
+        print(f"[case] many #{t}: n={n} depth={depth} n_cand={nc} grid={grid}", flush=True)
+        _check(lp[None], n, depth)
