@@ -102,7 +102,7 @@ __device__ __forceinline__ BtProbe bt_probe(const double* row, int nc) {
 __device__ __forceinline__ int bt_count(const double* row, int nc, double sv, double tau, const BtProbe& q) {
   int m = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) m += (q.span * (k + 1) - 1 < nc) & (sv + q.p[k] >= tau) ? 1 : 0;
+  for (int k = 0; k < 8; ++k) m += int((q.span * (k + 1) - 1 < nc) & (sv + q.p[k] >= tau));
   int c = q.span * m;
   for (int span = q.span >> 3; span >= 1; span >>= 3) {
     double x[8];
@@ -110,7 +110,7 @@ __device__ __forceinline__ int bt_count(const double* row, int nc, double sv, do
     for (int k = 0; k < 8; ++k) x[k] = row[min(c + span * (k + 1) - 1, nc - 1)];
     m = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m += (c + span * (k + 1) - 1 < nc) & (sv + x[k] >= tau) ? 1 : 0;
+    for (int k = 0; k < 8; ++k) m += int((c + span * (k + 1) - 1 < nc) & (sv + x[k] >= tau));
     c += span * m;
   }
   return c;

@@ -1194,13 +1194,11 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   constexpr int DB = D / 32, QN = D / 16;
   constexpr int LPW = RG::SEGS / NW;  // 1 KB copies per wave per stage
   static_assert(LPW * NW == RG::SEGS && LPW >= 1, "ring split over the waves");
-  constexpr int QB4 = 4 * D * 2;      // score operand rows: qbar hi, mid, lo and a zero row
   constexpr int QSF = D + (NT / D) * D;  // qbar scratch: the sum, then one partial per pair phase
-  constexpr int LDS = RG::MAIN + RG::PT_CAP * 4 + QSF * 4 + QB4;
+  constexpr int LDS = RG::MAIN + RG::PT_CAP * 4 + QSF * 4;
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   int* pt_lds = reinterpret_cast<int*>(smem + RG::MAIN);
   float* qs = reinterpret_cast<float*>(smem + RG::MAIN + RG::PT_CAP * 4);
-  T* qbt = reinterpret_cast<T*>(smem + RG::MAIN + RG::PT_CAP * 4 + QSF * 4);
 
   // ---- workgroup -> (sequence, KV head, chunk, row block).  Chunk c of
   // (b, g) runs on XCD (c + b Hkv + g) % 8 (blockIdx % 8 picks the XCD): every
@@ -1330,7 +1328,7 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
     for (int w = 0; w < kAncWords; ++w) anc[w] = a.ws_anc[((long long)b * a.N + t_node) * kAncWords + w];
   }
 
-  // ---- score operand: scale * qbar_g split into bf16 hi + mid + lo (B columns 0..2)
+  // ---- score operand: scale * qbar_g in fp32 (qs[0 .. D))
   const bool wg_scores = a.do_scores && c0 < Pb;
   if (wg_scores) {
     if (a.prep_qbar) {
@@ -1376,17 +1374,7 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
         qs[tid] = sacc;
       }
     }
-    __syncthreads();
-    for (int d = tid; d < D; d += NT) {
-      const float x = qs[d] * a.scale;
-      const bf16 hi = (bf16)x;
-      const float r1 = x - (float)hi;
-      const bf16 mid = (bf16)r1;
-      qbt[d] = hi;
-      qbt[D + d] = mid;
-      qbt[2 * D + d] = (bf16)(r1 - (float)mid);
-      qbt[3 * D + d] = (bf16)0.f;
-    }
+    if (tid < D) qs[tid] *= a.scale;  // the entry this thread wrote
     __syncthreads();
   }
 
@@ -1406,7 +1394,6 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
 #pragma unroll
     for (int hl = 0; hl < 2; ++hl)
       voff[db][hl] = tile_off<T, D>(4 * h + e4 + 8 * hl, 4 * db + 2 * dh + (cq >> 1)) + (cq & 1) * 8;
-  const int qb_row = lane32 < 3 ? lane32 : 3;
 
   f32x16 o[DB];
 #pragma unroll
@@ -1418,8 +1405,9 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   // two blocks' S^T products, one max and one rescale decision for the
   // stage's 64 keys, and both blocks' exponentials and P V products in one
   // branch-free stretch (so the second block's exponentials can issue while
-  // the first block's P V products run on the matrix cores).  The block
-  // scores this wave owns come last, from K fragments read again.  Stages
+  // the first block's P V products run on the matrix cores).  The stage's
+  // scores come last, eight keys per wave, when this row block owns the
+  // stage (K rows read again from the ring).  Stages
   // whose keys all lie in the prefix need no mask and run a copy of the body
   // without it; stages past the chunk end (the last one of a chunk) skip
   // their missing blocks.
@@ -1516,29 +1504,41 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
     }
     l += psum;
 
-    // block scores owned by this wave: scale * k . qbar over columns 0 + 1 + 2
-    // of the score operand, summed by lanes 0 and 32, which hold keys kappa(v, h)
-    if (wg_scores) {
+    // scores of the stage's prefix keys, by one row block per stage (stage s by
+    // row block s mod RB) and spread over all its waves, so no wave waits for
+    // another at the next barrier: wave w takes keys 8w .. 8w + 7 of the
+    // stage, each key's CPR lanes dot 8 of its dimensions with scale * qbar in
+    // fp32, the row shifts sum the CPR products, and the key's last lane writes
+    // the score (keys past P_b land in the row's padding and are never read)
+    if (wg_scores && (kst / RG::SK) % a.RB == rb) {
+      constexpr int CPR = D / 8, KPR = 64 / CPR;  // lanes per key, keys per 16-byte read
+      static_assert(NW * 8 == RG::SK && KPR <= 8 && 8 % KPR == 0, "eight keys per wave");
+      const int kw = kst + 8 * wave;
+      if (kw < Pb && kw < c1) {
+        const int cc = lane % CPR;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(qs + 8 * cc);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(qs + 8 * cc + 4);
+        float acc[8 / KPR];
 #pragma unroll
-      for (int kb = 0; kb < RG::NB; ++kb) {
-        if (!FULL && kb >= nb) break;
-        const int kb0 = kst + 32 * kb;
-        const int jblk = kb0 >> 5;
-        if (!(kb0 < Pb && (jblk % a.RB) == rb && ((jblk / a.RB) % NW) == wave)) continue;
-        const char* Kb = Kt + kb * 32 * RG::ROWB;
-        f32x16 sc = f32x16{};
+        for (int j = 0; j < 8 / KPR; ++j) {
+          const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Kt + tile_off<T, D>(8 * wave + KPR * j + lane / CPR, cc));
+          float d = (float)kv[0] * x0[0];
+          d = __builtin_fmaf((float)kv[1], x0[1], d);
+          d = __builtin_fmaf((float)kv[2], x0[2], d);
+          d = __builtin_fmaf((float)kv[3], x0[3], d);
+          d = __builtin_fmaf((float)kv[4], x1[0], d);
+          d = __builtin_fmaf((float)kv[5], x1[1], d);
+          d = __builtin_fmaf((float)kv[6], x1[2], d);
+          acc[j] = __builtin_fmaf((float)kv[7], x1[3], d);
+        }
 #pragma unroll
-        for (int ks = 0; ks < QN; ++ks)
-          sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(Kb + koff[ks]),
-                         *reinterpret_cast<const bf16x8*>(qbt + qb_row * D + 16 * ks + 8 * h), sc);
-        float tv[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tv[v] = sc[v] + row_shl<1>(sc[v]) + row_shl<2>(sc[v]);
-        if (lane32 == 0) {  // whole block (rows are padded by 32; entries past P_b are never read)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<f32x4*>(sdst + kb0 + 8 * qd + 4 * h) =
-                f32x4{tv[4 * qd], tv[4 * qd + 1], tv[4 * qd + 2], tv[4 * qd + 3]};
+        for (int j = 0; j < 8 / KPR; ++j) {
+          float v = acc[j];  // inclusive sums over the row of 16 lanes, 1 + 2 + 4 (+ 8)
+          v += dpp_f<0x111, 0xf>(0.f, v);
+          v += dpp_f<0x112, 0xf>(0.f, v);
+          v += dpp_f<0x114, 0xf>(0.f, v);
+          if constexpr (CPR == 16) v += dpp_f<0x118, 0xf>(0.f, v);
+          if (cc == CPR - 1) sdst[kw + KPR * j + lane / CPR] = v;
         }
       }
     }
