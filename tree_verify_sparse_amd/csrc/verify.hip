@@ -17,10 +17,12 @@
 //                    comes straight from the row-major tile via transpose reads).
 // The score needs sum over rows and heads of the logits, which is linear in
 // q: s_i = scale * k_i . qbar_g with qbar_g the fp32 sum of the scoring rows'
-// queries of KV head g.  It is computed in the same K pass as extra MFMA
-// columns of S^T holding qbar split into three bf16 parts (hi + mid + lo
-// carries qbar to fp32 precision; bf16 x bf16 products are exact in fp32), so
-// only one fp32 per prefix key and KV head leaves the kernel.
+// queries of KV head g.  It is computed in the same K pass, so only one fp32
+// per prefix key and KV head leaves the kernel: as extra MFMA columns of S^T
+// holding qbar split into three bf16 parts (hi + mid + lo carries qbar to fp32
+// precision; bf16 x bf16 products are exact in fp32) in the generic and the
+// streaming kernels, and as fp32 dot products on the vector unit, spread over
+// all eight waves, in the tree kernel.
 // Partial (m, l, o) per chunk are merged with log-sum-exp weights by a second
 // kernel, which also sums the per-KV-head score partials in a fixed order.
 #include "select_dev.h"
