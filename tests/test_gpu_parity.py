@@ -91,6 +91,12 @@ CASES = {
     "tree64_paged_ps24": lambda: make_custom(
         seed=121, B=2, Hq=32, Hkv=8, D=128, dtype="bf16", P=[2100, 333], N=64, tree="best_first", tree_depth=6,
         score_rows="all", k_sel=64, layout="paged", page_size=24, q_std_mult=4.0, v_canary=8.0),
+    # head_dim 64 tree kernel with two row blocks per KV head (400 rows): the
+    # prefix stages' scores alternate between the row blocks (eight keys per
+    # wave, eight lanes per key), with a subset of scoring rows
+    "tree100_bf16_d64_rb2": lambda: make_custom(
+        seed=123, B=1, Hq=16, Hkv=4, D=64, dtype="bf16", P=3001, N=100, tree="best_first", tree_depth=7,
+        score_rows=[0, 5, 17, 42, 99], k_sel=150, q_std_mult=3.0),
     "f32_chain_paged_ps24": lambda: make_custom(
         seed=122, B=2, Hq=8, Hkv=2, D=64, dtype="f32", P=[900, 250], N=5, score_rows="all", k_sel=40,
         layout="paged", page_size=24, q_std_mult=4.0),
