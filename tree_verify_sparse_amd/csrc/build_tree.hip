@@ -82,7 +82,9 @@ __device__ __forceinline__ double next_up(double x) {
 }
 
 // The first step of the search over a depth's sorted list: span and the
-// eight probes (the same for every parent of the level, so loaded once).
+// eight probes (the same for every parent of the level, so loaded once).  The
+// steps of spans 64, 8 and 1 reach rank 583, past the 256 ranks a depth may
+// hold (sv_build_tree rejects more), so every count is exact.
 struct BtProbe {
   int span;
   double p[8];
