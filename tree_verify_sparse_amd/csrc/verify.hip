@@ -81,7 +81,6 @@ struct VerifyArgs {
   const void* q;
   void* out;
   KvView kv;
-  const int32_t* prefix_len;
   float* ws_o;
   f32x2* ws_ml;
   float* ws_s;
@@ -89,7 +88,12 @@ struct VerifyArgs {
   uint32_t* ws_anc;
   const int32_t* parent;
   float* scores;
+  const int32_t* sel_k;  // device [B] requested k, or null: no selection (see below)
+  // bytes 128..191: what a verify kernel reads before its first copies, in one
+  // 64-byte line of the argument block (with kv above: two lines in all)
+  const int32_t* prefix_len;
   int B, N, Hq, Hkv, G, R, RB, Rpad, P_max, chunk, n_chunks, n_units;
+  int len_bias;  // 0 for verification; -1 for a decode over rows [0, prefix_len[b]) (see seq_prefix)
   int tree, do_scores, prep_qbar;
   int qsplit;  // prep_qbar: partial sums per (sequence, KV head), each over kQbarPairs (row, head) pairs
   int s_stride;  // row stride of the per-KV-head score partials: P_max + 32 (whole blocks are stored), rounded up to 4
@@ -97,11 +101,9 @@ struct VerifyArgs {
   int ps_shift;  // log2(page_size) if it is a power of two, else -1
   float scale, scale_log2;
   int n_score_rows;
-  int len_bias;  // 0 for verification; -1 for a decode over rows [0, prefix_len[b]) (see seq_prefix)
   int head_scores;  // 1: scores are per KV head, [B][Hkv][P_max] (no sum over the groups)
   // fused selection (sv_verify_select): the merge's score workgroups run the
   // two selection passes on the scores they sum (select_dev.h)
-  const int32_t* sel_k;  // device [B] requested k, or null: no selection
   int sel_kmax;
   int32_t* sel_idx;      // [B][sel_kmax]
   int32_t* sel_count;    // [B] or null
@@ -111,6 +113,8 @@ struct VerifyArgs {
 
 
 
+static_assert(offsetof(VerifyArgs, prefix_len) == 128 && offsetof(VerifyArgs, len_bias) + 4 <= 192,
+              "the fields read first share one 64-byte line");
 // P_b of sequence b, clamped to [0, P_max], and in *L the length of its KV
 // range P_b + N.  A decode over the first n rows of a dense buffer passes n
 // with len_bias -1 and N = 1: the query is the last row's token and sees
@@ -733,21 +737,40 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
   // c % 8 (blockIdx % 8 picks the XCD), so every XCD gets a slice of every
   // sequence and head whatever the lengths.  One sequence: each XCD streams
   // whole heads (consecutive chunks), which measured slightly faster.
+  // Every argument the first copies need is read here, before anything
+  // branches, so the loads go out together: each one first read behind a
+  // branch or a division was its own trip to memory (the argument block is
+  // not in the scalar cache when a launch starts).
+  const int aB = a.B, aHkv = a.Hkv, ach = a.n_chunks, anu = a.n_units, aN = a.N, aPmax = a.P_max,
+            alb = a.len_bias;
+  const int32_t* apl = a.prefix_len;
+  const char* kbase = reinterpret_cast<const char*>(a.kv.k);
+  const char* vbase = reinterpret_cast<const char*>(a.kv.v);
+  const long long sstr = a.kv.seq_stride, nslots = a.kv.num_slots;
+  // used here, so that their line of the argument block comes with the first
+  // trip (the test never fires: the host rejects null caches)
+  if (kbase == nullptr || nslots <= 0 || aB <= 0 || ach <= 0) return;
   int c, g, b;
-  if (a.B > 1) {
-    c = (int)(blockIdx.x >> 3) / (a.B * a.Hkv) * 8 + (int)(blockIdx.x & 7);
-    g = (int)(blockIdx.x >> 3) % a.Hkv;
-    b = (int)(blockIdx.x >> 3) / a.Hkv % a.B;
-    if (c >= a.n_chunks) return;
+  if (aB > 1) {
+    c = (int)(blockIdx.x >> 3) / (aB * aHkv) * 8 + (int)(blockIdx.x & 7);
+    g = (int)(blockIdx.x >> 3) % aHkv;
+    b = (int)(blockIdx.x >> 3) / aHkv % aB;
+    if (c >= ach) return;
   } else {
-    const int lid = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
-    if (lid >= a.n_units) return;
-    c = lid % a.n_chunks;
-    g = lid / a.n_chunks;
+    // one sequence: the grid holds the units rounded up to whole XCD rows
+    const int lid = (int)(blockIdx.x & 7) * ((anu + 7) >> 3) + (int)(blockIdx.x >> 3);
+    if (lid >= anu) return;
+    c = lid % ach;
+    g = lid / ach;
     b = 0;
   }
-  int L;
-  const int Pb = seq_prefix(a, b, &L);
+  int L, Pb;
+  {
+    int x = apl[b] + alb;
+    const bool empty = alb < 0 && x < 0;
+    Pb = x < 0 ? 0 : (x > aPmax ? aPmax : x);
+    L = empty ? 0 : Pb + aN;
+  }
   const int nbk = (L + 31) >> 5;
 
   const int tid = threadIdx.x;
@@ -755,7 +778,7 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
   const int lane = tid & 63, lane32 = lane & 31, h = lane >> 5;
 
   // balanced split of the sequence's blocks over all waves of all its chunks
-  const long long WT = (long long)a.n_chunks * 4;
+  const long long WT = (long long)ach * 4;
   const int blk0 = (int)((long long)(c * 4 + wave) * nbk / WT);
   const int blk1 = (int)((long long)(c * 4 + wave + 1) * nbk / WT);
   const int cblk0 = (int)((long long)c * 4 * nbk / WT);
@@ -778,7 +801,7 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
     }
     __syncthreads();
   }
-  const long long seq_base = (long long)b * a.kv.seq_stride;
+  const long long seq_base = (long long)b * sstr;
   // slot of a position: page entries from the cached slice (FROM_MEM: pages
   // past it are read from memory; the copy paths keep the two apart, so the
   // common one never waits on a memory read, which would also wait for every
@@ -806,8 +829,8 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem) +
       (uint32_t)(wave * WRg::WAVE);
   const long long slot_bytes = (long long)a.Hkv * WRg::ROWB;
-  const char* kg = reinterpret_cast<const char*>(a.kv.k) + (long long)g * WRg::ROWB;
-  const char* vg = reinterpret_cast<const char*>(a.kv.v) + (long long)g * WRg::ROWB;
+  const char* kg = kbase + (long long)g * WRg::ROWB;
+  const char* vg = vbase + (long long)g * WRg::ROWB;
   uint32_t doff[WRg::LPT];  // per-lane offset of copy j inside a contiguous block
   int drow[WRg::LPT], dcol[WRg::LPT];
 #pragma unroll
@@ -821,7 +844,7 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
     const int key0 = blk * 32;
     const uint32_t ld = ring_l + (uint32_t)(st * WRg::BLK + (is_v ? WRg::TILE : 0));
     const char* tg = is_v ? vg : kg;
-    if (!PAGED && key0 + 32 <= L && seq_base + key0 + 32 <= a.kv.num_slots) {
+    if (!PAGED && key0 + 32 <= L && seq_base + key0 + 32 <= nslots) {
       const char* bt = tg + (seq_base + key0) * slot_bytes;
 #pragma unroll
       for (int j = 0; j < WRg::LPT; ++j) dma16_sbase(ld + j * 1024, doff[j], bt);
