@@ -103,8 +103,8 @@ __device__ __forceinline__ int sel_seg_start(int t, int P, int seg, int nseg) {
 __device__ __forceinline__ void sel_row_sizes(const int32_t* prefix_len, const int32_t* kreq, int b, int P_max,
                                               int k_max, int* P, int* k) {
   int p = prefix_len[b];
+  int kk = kreq[b];  // both loads in flight before either is used
   p = p < 0 ? 0 : (p > P_max ? P_max : p);
-  int kk = kreq[b];
   kk = kk < 0 ? 0 : kk;
   kk = kk > p ? p : kk;
   kk = kk > k_max ? k_max : kk;
