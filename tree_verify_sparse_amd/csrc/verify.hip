@@ -1224,6 +1224,10 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   int* pt_lds = reinterpret_cast<int*>(smem + RG::MAIN);
   float* qs = reinterpret_cast<float*>(smem + RG::MAIN + RG::PT_CAP * 4);
+  // one field from each line of the argument block the prologue reads, so the
+  // lines arrive in one trip instead of one after another (each first read
+  // behind a branch or a division waited for its own)
+  asm volatile("" ::"v"(a.B), "v"((uint32_t)(uintptr_t)a.q), "v"((uint32_t)(uintptr_t)a.ws_anc), "v"(a.do_scores));
 
   // ---- workgroup -> (sequence, KV head, chunk, row block).  Chunk c of
   // (b, g) runs on XCD (c + b Hkv + g) % 8 (blockIdx % 8 picks the XCD): every
@@ -1843,6 +1847,10 @@ __global__ void __launch_bounds__(256) verify_prep(const VerifyArgs a, int n_qba
   __shared__ float part[256];
   __shared__ __attribute__((aligned(16))) uint32_t ancs[kMaxNodes][kAncWords];
   __shared__ int jmp[kMaxNodes];
+  // one field from each line of the argument block either path reads first,
+  // so the lines arrive in one trip instead of one after another
+  asm volatile("" ::"v"(n_qbar_wgs), "v"(a.N), "v"((uint32_t)(uintptr_t)a.q), "v"((uint32_t)(uintptr_t)a.ws_anc),
+               "v"(a.qsplit));
   if ((int)blockIdx.x < n_qbar_wgs) {
     // partial qbar of (b, g) over pairs [sp * kQbarPairs, (sp + 1) * kQbarPairs):
     // D columns x (256 / D) pair phases; every load of the thread is issued
