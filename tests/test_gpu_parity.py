@@ -117,7 +117,12 @@ def _oracle(wl, with_attention=True):
 @pytest.mark.parametrize("name", list(CASES))
 def test_verify_and_step_parity(name):
     print(f"[case] {name}", flush=True)
-    wl = CASES[name]()
+    check_workload(CASES[name]())
+
+
+def check_workload(wl):
+    """Verification outputs, scores, the selection and the draft steps of one
+    workload against the oracle."""
     dw = DevWorkload(wl)
     ref = _oracle(wl)
     out, scores = dw.verify()
