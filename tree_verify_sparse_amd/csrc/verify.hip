@@ -1211,6 +1211,23 @@ __global__ void __launch_bounds__(256) verify_stream(const VerifyArgs a) {
 // waves hold the same rows, so each writes its own (m, l, o) partials.
 constexpr int kTreeWaves = 8;
 
+// Inclusive prefix sum over the 64 lanes (DPP row shifts, then the row
+// broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += (int)__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += (int)__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += (int)__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += (int)__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += (int)__builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += (int)__builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+// The lowest lane whose x exceeds v (x non-decreasing over the lanes; 64 if none).
+__device__ __forceinline__ int first_lane_above(int x, int v) {
+  const unsigned long long m = __ballot(x > v);
+  return m ? __builtin_ctzll(m) : 64;
+}
+
 template <int D, bool PAGED>
 __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs a) {
   using T = bf16;
@@ -1229,22 +1246,55 @@ __global__ void __launch_bounds__(64 * kTreeWaves) verify_tree(const VerifyArgs 
   // behind a branch or a division waited for its own)
   asm volatile("" ::"v"(a.B), "v"((uint32_t)(uintptr_t)a.q), "v"((uint32_t)(uintptr_t)a.ws_anc), "v"(a.do_scores));
 
-  // ---- workgroup -> (sequence, KV head, chunk, row block).  Chunk c of
-  // (b, g) runs on XCD (c + b Hkv + g) % 8 (blockIdx % 8 picks the XCD): every
-  // XCD gets a slice of every sequence and head, and the chunks past a
-  // multiple of 8 -- a sequence's chunk count depends on its length -- start
-  // on a different XCD for each (sequence, head), so no XCD collects them
-  // (chunk c on XCD c % 8 gave XCD 0 45% more work than XCD 7 on a batch of
-  // 16 mixed lengths).  The row blocks of a chunk, which read the same K/V,
+  // ---- workgroup -> (sequence, KV head, chunk, row block); blockIdx % 8
+  // picks the XCD, and the row blocks of a chunk, which read the same K/V,
   // share that XCD's L2.
-  int wk = (int)(blockIdx.x >> 3);
-  const int rb = wk % a.RB;
-  wk /= a.RB;
-  const int g = wk % a.Hkv;
-  wk /= a.Hkv;
-  const int b = wk % a.B;
-  const int c = wk / a.B * 8 + (((int)(blockIdx.x & 7) - b * a.Hkv - g) & 7);
-  if (c >= a.n_chunks) return;
+  int rb, g, b, c;
+  if (a.B <= 64) {
+    // Batches of up to 64 sequences: every sequence's whole chunks first, then
+    // the shorter last chunks.  The dispatcher starts workgroups in grid order,
+    // so the short ones run last and fill the final round instead of leaving
+    // CUs idle behind the last whole chunks.  Item j = (blockIdx / 8 / RB) * 8
+    // + blockIdx % 8 runs on XCD j % 8, and the RB row blocks of one item share
+    // that XCD's L2.
+    const int s8 = (int)(blockIdx.x >> 3);
+    rb = s8 % a.RB;
+    const int j = s8 / a.RB * 8 + (int)(blockIdx.x & 7);
+    const int ln = (int)(threadIdx.x & 63);
+    int Lb = 0;
+    if (ln < a.B) seq_prefix(a, ln, &Lb);
+    const int nf = Lb / a.chunk;                         // whole chunks of sequence ln
+    const int tl = Lb > nf * a.chunk ? 1 : 0;            // and a shorter last one
+    const int fi = wave_incl_sum(nf * a.Hkv);
+    const int F = __builtin_amdgcn_readlane(fi, 63);
+    if (j < F) {
+      b = first_lane_above(fi, j);
+      const int r = j - (__builtin_amdgcn_readlane(fi, b) - __builtin_amdgcn_readlane(nf, b) * a.Hkv);
+      c = r / a.Hkv;
+      g = (r - c * a.Hkv + c) % a.Hkv;  // heads rotated by the chunk: each XCD sees every head
+    } else {
+      const int ti = wave_incl_sum(tl * a.Hkv);
+      const int jt = j - F;
+      if (jt >= __builtin_amdgcn_readlane(ti, 63)) return;
+      b = first_lane_above(ti, jt);
+      g = jt - (__builtin_amdgcn_readlane(ti, b) - __builtin_amdgcn_readlane(tl, b) * a.Hkv);
+      c = __builtin_amdgcn_readlane(nf, b);
+    }
+  } else {
+    // Larger batches: chunk c of (b, g) runs on XCD (c + b Hkv + g) % 8, so
+    // every XCD gets a slice of every sequence and head, and the chunks past a
+    // multiple of 8 start on a different XCD for each (sequence, head) (chunk c
+    // on XCD c % 8 gave XCD 0 45% more work than XCD 7 on a batch of 16 mixed
+    // lengths).
+    int wk = (int)(blockIdx.x >> 3);
+    rb = wk % a.RB;
+    wk /= a.RB;
+    g = wk % a.Hkv;
+    wk /= a.Hkv;
+    b = wk % a.B;
+    c = wk / a.B * 8 + (((int)(blockIdx.x & 7) - b * a.Hkv - g) & 7);
+    if (c >= a.n_chunks) return;
+  }
   int L;
   const int Pb = seq_prefix(a, b, &L);
   // fixed-length chunks (a whole number of stages): a sequence shorter than the
